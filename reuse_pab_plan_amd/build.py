@@ -1,0 +1,94 @@
+"""Build libpab.so in-tree with hipcc for gfx950.
+
+    python -m reuse_pab_plan_amd.build [--jobs N]
+
+Every source under ``csrc/`` is compiled to ``_build/`` (at the repository
+root) and linked into ``reuse_pab_plan_amd/libpab.so``.  The build always
+recompiles: it is also the "does it build" check.  No GPU is needed.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpab.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = [
+    "abi.cpp",
+    "plan.cpp",
+    "dispatch.cpp",
+    "mse.hip",
+    "attn_f32.hip",
+    "spatial.hip",
+    "cross.hip",
+    "temporal.hip",
+]
+
+# Packed fp32 instructions are disabled for all device code on purpose.
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src: str) -> tuple[str, float, str]:
+    t0 = time.time()
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(
+        line for line in (res.stdout + res.stderr).splitlines()
+        if "packed-fp32-ops" not in line  # host pass does not know the device feature
+    )
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{out}")
+    return obj, time.time() - t0, out
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for (obj, dt, out), src in zip(results, SOURCES):
+        if verbose:
+            print(f"[build] {src:16s} {dt:6.1f}s", flush=True)
+        if out.strip() and verbose:
+            print(out, flush=True)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[r[0] for r in results]]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"[build] wrote {LIB}", flush=True)
+    return LIB
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=None)
+    args = ap.parse_args(argv)
+    build(args.jobs)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

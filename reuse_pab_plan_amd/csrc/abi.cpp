@@ -1,0 +1,239 @@
+// abi.cpp -- exported attention and MSE entry points: argument validation
+// (before any HIP call), error text, and dispatch to the kernel launchers.
+#include "abi.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+
+namespace pab {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // sanity bound on tensor sizes
+
+bool dims_ok(std::initializer_list<int64_t> dims, int64_t* total) {
+  int64_t t = 1;
+  for (int64_t d : dims) {
+    if (d <= 0) return false;
+    if (t > kMaxElems / d) return false;
+    t *= d;
+  }
+  *total = t;
+  return true;
+}
+
+bool d_supported(int32_t D) { return D >= 8 && D <= 128 && D % 8 == 0; }
+
+std::string fmt(const char* f, ...) __attribute__((format(printf, 1, 2)));
+std::string fmt(const char* f, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, f);
+  vsnprintf(buf, sizeof buf, f, ap);
+  va_end(ap);
+  return buf;
+}
+}  // namespace
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+int ok() {
+  g_last_error.clear();
+  return PAB_OK;
+}
+int device_error(const char* what, int hip_err) {
+  return fail(PAB_ERR_DEVICE, fmt("%s: HIP error %d (%s)", what, hip_err,
+                                  hipGetErrorString((hipError_t)hip_err)));
+}
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+size_t dtype_size(int32_t dtype) { return dtype == PAB_BF16 ? 2 : (dtype == PAB_F32 ? 4 : 0); }
+
+static int check_common(const char* fn, int32_t D, int32_t dtype, float scale) {
+  if (dtype != PAB_BF16 && dtype != PAB_F32)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: unsupported dtype %d", fn, dtype));
+  if (!d_supported(D))
+    return fail(PAB_ERR_UNSUPPORTED,
+                fmt("%s: head dim D=%d unsupported (need a multiple of 8 in [8, 128])", fn, D));
+  if (!(scale >= 0.f) || !std::isfinite(scale))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: softmax_scale must be finite and >= 0", fn));
+  return PAB_OK;
+}
+
+int check_video_attn(const char* fn, const void* q, const void* k, const void* v, const void* o,
+                     int32_t B, int32_t H, int32_t F, int32_t S, int32_t D, int32_t dtype,
+                     float scale, bool temporal) {
+  if (!q || !k || !v || !o) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
+  int64_t n = 0;
+  if (!dims_ok({B, H, F, S, D}, &n))
+    return fail(PAB_ERR_INVALID_ARG,
+                fmt("%s: bad shape B=%d H=%d F=%d S=%d D=%d", fn, B, H, F, S, D));
+  int st = check_common(fn, D, dtype, scale);
+  if (st) return st;
+  if (temporal && F > 64)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: F=%d frames unsupported (max 64)", fn, F));
+  const size_t bytes = (size_t)n * dtype_size(dtype);
+  if (ranges_overlap(o, bytes, q, bytes) || ranges_overlap(o, bytes, k, bytes) ||
+      ranges_overlap(o, bytes, v, bytes))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: output overlaps an input", fn));
+  return PAB_OK;
+}
+
+int check_cross_attn(const void* q, const void* kt, const void* vt, const void* o, int32_t B,
+                     int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale) {
+  const char* fn = "pab_attn_cross";
+  if (!q || !kt || !vt || !o) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
+  if (!aligned16(q) || !aligned16(kt) || !aligned16(vt) || !aligned16(o))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
+  int64_t nq_el = 0, nk_el = 0;
+  if (!dims_ok({B, H, Nq, D}, &nq_el) || !dims_ok({B, H, L, D}, &nk_el))
+    return fail(PAB_ERR_INVALID_ARG,
+                fmt("%s: bad shape B=%d H=%d Nq=%lld L=%d D=%d", fn, B, H, (long long)Nq, L, D));
+  int st = check_common(fn, D, dtype, scale);
+  if (st) return st;
+  if (L > 128) return fail(PAB_ERR_UNSUPPORTED, fmt("%s: L=%d text tokens unsupported (max 128)", fn, L));
+  if (Nq > ((int64_t)1 << 31) * 32)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: Nq too large", fn));
+  const size_t es = dtype_size(dtype);
+  const size_t qb = (size_t)nq_el * es, kb = (size_t)nk_el * es;
+  if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, kt, kb) || ranges_overlap(o, qb, vt, kb))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: output overlaps an input", fn));
+  return PAB_OK;
+}
+
+int check_mse(const void* a, const void* b, int64_t n, int32_t dtype, const double* out,
+              const void* ws, size_t ws_bytes) {
+  const char* fn = "pab_attn_diff_mse";
+  if (!a || !b || !out || !ws) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
+  if (!aligned16(a) || !aligned16(b) || !aligned16(ws) || ((uintptr_t)out & 7u))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: misaligned pointer", fn));
+  if (n < 1 || n > kMaxElems) return fail(PAB_ERR_INVALID_ARG, fmt("%s: bad n=%lld", fn, (long long)n));
+  if (dtype != PAB_BF16 && dtype != PAB_F32)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: unsupported dtype %d", fn, dtype));
+  const size_t need = pab_mse_workspace_bytes(n);
+  if (ws_bytes < need)
+    return fail(PAB_ERR_CAPACITY, fmt("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need));
+  return PAB_OK;
+}
+
+static float resolve_scale(float scale, int32_t D) {
+  return scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
+}
+
+int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
+                int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream) {
+  const float c = resolve_scale(scale, D);
+  hipError_t e;
+  if (dtype == PAB_BF16) {
+    e = launch_spatial_bf16(q, k, v, o, (int64_t)B * H * F, S, D, c, (hipStream_t)stream);
+  } else {
+    SeqLayout lay{(int64_t)B * H * F, 1, (int64_t)S * D, 0, D, (int64_t)S * D, 0, D, S, S};
+    e = launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lay, D, c,
+                        (hipStream_t)stream);
+  }
+  return e == hipSuccess ? ok() : device_error("pab_attn_spatial launch", e);
+}
+
+int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
+                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream) {
+  const float c = resolve_scale(scale, D);
+  hipError_t e;
+  if (dtype == PAB_BF16) {
+    e = launch_temporal_bf16(q, k, v, o, (int64_t)B * H, F, S, D, c, (hipStream_t)stream);
+  } else {
+    const int64_t fs = (int64_t)F * S * D;
+    SeqLayout lay{(int64_t)B * H * S, S, fs, D, (int64_t)S * D, fs, D, (int64_t)S * D, F, F};
+    e = launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lay, D, c,
+                        (hipStream_t)stream);
+  }
+  return e == hipSuccess ? ok() : device_error("pab_attn_temporal launch", e);
+}
+
+int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B, int32_t H,
+              int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale, void* stream) {
+  const float c = resolve_scale(scale, D);
+  hipError_t e;
+  if (dtype == PAB_BF16) {
+    e = launch_cross_bf16(q, kt, vt, o, (int64_t)B * H, Nq, L, D, c, (hipStream_t)stream);
+  } else {
+    SeqLayout lay{(int64_t)B * H, 1, Nq * D, 0, D, (int64_t)L * D, 0, D, Nq, L};
+    e = launch_attn_f32((const float*)q, (const float*)kt, (const float*)vt, (float*)o, lay, D, c,
+                        (hipStream_t)stream);
+  }
+  return e == hipSuccess ? ok() : device_error("pab_attn_cross launch", e);
+}
+
+int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out, void* ws,
+            void* stream) {
+  hipError_t e = launch_mse(a, b, n, dtype, out, (double*)ws, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : device_error("pab_attn_diff_mse launch", e);
+}
+
+}  // namespace pab
+
+using namespace pab;
+
+extern "C" {
+
+int pab_attn_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
+                     int32_t F, int32_t S, int32_t D, int32_t dtype, float softmax_scale,
+                     void* stream) {
+  int st = check_video_attn("pab_attn_spatial", q, k, v, o, B, H, F, S, D, dtype, softmax_scale, false);
+  if (st) return st;
+  return run_spatial(q, k, v, o, B, H, F, S, D, dtype, softmax_scale, stream);
+}
+
+int pab_attn_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
+                      int32_t F, int32_t S, int32_t D, int32_t dtype, float softmax_scale,
+                      void* stream) {
+  int st = check_video_attn("pab_attn_temporal", q, k, v, o, B, H, F, S, D, dtype, softmax_scale, true);
+  if (st) return st;
+  return run_temporal(q, k, v, o, B, H, F, S, D, dtype, softmax_scale, stream);
+}
+
+int pab_attn_cross(const void* q, const void* k_text, const void* v_text, void* o, int32_t B,
+                   int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype,
+                   float softmax_scale, void* stream) {
+  int st = check_cross_attn(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale);
+  if (st) return st;
+  return run_cross(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale, stream);
+}
+
+size_t pab_mse_workspace_bytes(int64_t n) {
+  if (n < 1) return 0;
+  // Enough partials for either dtype's grid, rounded to 256 bytes.
+  const int blocks = mse_num_blocks(n, PAB_F32) > mse_num_blocks(n, PAB_BF16)
+                         ? mse_num_blocks(n, PAB_F32)
+                         : mse_num_blocks(n, PAB_BF16);
+  return ((size_t)blocks * sizeof(double) + 255) / 256 * 256;
+}
+
+int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out_dev,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mse(a, b, n, dtype, out_dev, workspace, workspace_bytes);
+  if (st) return st;
+  return run_mse(a, b, n, dtype, out_dev, workspace, stream);
+}
+
+const char* pab_last_error(void) { return g_last_error.c_str(); }
+
+const char* pab_version(void) { return "pab-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

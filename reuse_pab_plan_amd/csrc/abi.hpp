@@ -1,0 +1,41 @@
+// abi.hpp -- internal helpers of the C ABI layer: the thread-local error
+// text and the argument checks shared by the entry points.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/pab.h"
+
+namespace pab {
+
+int fail(int status, const std::string& msg);  // records msg, returns status
+int ok();                                       // clears the error, returns PAB_OK
+int device_error(const char* what, int hip_err);
+
+bool aligned16(const void* p);
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn);
+size_t dtype_size(int32_t dtype);
+
+// Validation of the attention calls, with no HIP call (shared by the direct
+// entry points and the step dispatcher).
+int check_video_attn(const char* fn, const void* q, const void* k, const void* v, const void* o,
+                     int32_t B, int32_t H, int32_t F, int32_t S, int32_t D, int32_t dtype,
+                     float scale, bool temporal);
+int check_cross_attn(const void* q, const void* kt, const void* vt, const void* o, int32_t B,
+                     int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale);
+int check_mse(const void* a, const void* b, int64_t n, int32_t dtype, const double* out,
+              const void* ws, size_t ws_bytes);
+
+// Launch without re-validating (arguments already checked).
+int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
+                int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream);
+int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
+                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream);
+int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B, int32_t H,
+              int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale, void* stream);
+int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out, void* ws,
+            void* stream);
+
+}  // namespace pab

@@ -1,0 +1,124 @@
+// dispatch.cpp -- one denoising step of one block under the broadcast cache.
+//
+// PAB article, Figure 2 caption: an attention result is broadcast to the
+// next few steps, which then skip the attention computation.  Here a type
+// that recomputes at this step launches its kernel into its next cache slot;
+// a type that reuses launches nothing at all, and the slot that its last
+// recompute wrote is handed back as this step's output (zero bytes moved,
+// bit-identical by construction).  With two slots per type the previous
+// output survives the recompute, so the attention difference between the two
+// (PAB article, Figure 1 caption: measured by the MSE) can be taken on the
+// device.  The dispatcher is stateless: slot parity is the number of
+// recomputes so far, read off the schedule.
+#include <stdint.h>
+
+#include "abi.hpp"
+
+using namespace pab;
+
+namespace {
+
+size_t output_elems(const pab_type_desc& t) {
+  return (size_t)t.B * t.H * t.F * t.S * t.D;
+}
+
+int check_type(const pab_step_desc* d, int a) {
+  const pab_type_desc& t = d->types[a];
+  const void* probe_out = t.slot[0];
+  int st;
+  switch (t.kind) {
+    case PAB_SPATIAL:
+      st = check_video_attn("pab_step_dispatch(spatial)", t.q, t.k, t.v, probe_out, t.B, t.H, t.F,
+                            t.S, t.D, d->dtype, d->softmax_scale, false);
+      break;
+    case PAB_TEMPORAL:
+      st = check_video_attn("pab_step_dispatch(temporal)", t.q, t.k, t.v, probe_out, t.B, t.H, t.F,
+                            t.S, t.D, d->dtype, d->softmax_scale, true);
+      break;
+    case PAB_CROSS:
+      st = check_cross_attn(t.q, t.k, t.v, probe_out, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D,
+                            d->dtype, d->softmax_scale);
+      break;
+    default:
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: unknown attention kind");
+  }
+  if (st) return st;
+  if (t.slot[1]) {
+    if (!aligned16(t.slot[1]))
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slot[1] must be 16-byte aligned");
+    const size_t bytes = output_elems(t) * dtype_size(d->dtype);
+    if (ranges_overlap(t.slot[0], bytes, t.slot[1], bytes))
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slots overlap");
+    const size_t qbytes = bytes;
+    if (ranges_overlap(t.slot[1], bytes, t.q, qbytes) ||
+        (t.kind != PAB_CROSS && (ranges_overlap(t.slot[1], bytes, t.k, qbytes) ||
+                                 ranges_overlap(t.slot[1], bytes, t.v, qbytes))))
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slot[1] overlaps an input");
+  }
+  if (t.drift && t.slot[1]) {
+    if ((uintptr_t)t.drift & 7u) return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: misaligned drift");
+    const int64_t n = (int64_t)output_elems(t);
+    if (!d->workspace || !aligned16(d->workspace))
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: drift needs a 16-byte aligned workspace");
+    if (d->workspace_bytes < pab_mse_workspace_bytes(n))
+      return fail(PAB_ERR_CAPACITY, "pab_step_dispatch: workspace too small for the drift MSE");
+  }
+  return PAB_OK;
+}
+
+}  // namespace
+
+extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32_t* recomputed_mask,
+                                 void** outputs) {
+  if (!desc || !desc->recompute || !desc->types)
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: NULL descriptor");
+  const int nt = desc->num_types;
+  if (nt < 1 || nt > 32) return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: num_types in [1, 32]");
+  if (desc->num_steps < 1 || step < 0 || step >= desc->num_steps)
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: step out of range");
+
+  // Slot of the latest output per type: recomputes in steps 0..step.
+  int32_t count[32];
+  for (int a = 0; a < nt; ++a) {
+    count[a] = 0;
+    for (int i = 0; i <= step; ++i) count[a] += desc->recompute[(size_t)i * nt + a] ? 1 : 0;
+    if (count[a] == 0)
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: type reused before any recompute");
+    int st = check_type(desc, a);
+    if (st) return st;
+  }
+
+  uint32_t mask = 0;
+  for (int a = 0; a < nt; ++a) {
+    const pab_type_desc& t = desc->types[a];
+    const bool two = t.slot[1] != nullptr;
+    void* cur = two ? t.slot[(count[a] - 1) & 1] : t.slot[0];
+    if (outputs) outputs[a] = cur;
+    if (!desc->recompute[(size_t)step * nt + a]) continue;  // broadcast: no work at all
+    mask |= 1u << a;
+    int st;
+    switch (t.kind) {
+      case PAB_SPATIAL:
+        st = run_spatial(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
+                         desc->softmax_scale, desc->stream);
+        break;
+      case PAB_TEMPORAL:
+        st = run_temporal(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
+                          desc->softmax_scale, desc->stream);
+        break;
+      default:
+        st = run_cross(t.q, t.k, t.v, cur, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D, desc->dtype,
+                       desc->softmax_scale, desc->stream);
+        break;
+    }
+    if (st) return st;
+    if (two && t.drift && count[a] >= 2) {
+      const void* prev = t.slot[count[a] & 1];
+      st = run_mse(cur, prev, (int64_t)output_elems(t), desc->dtype, t.drift + step,
+                   desc->workspace, desc->stream);
+      if (st) return st;
+    }
+  }
+  if (recomputed_mask) *recomputed_mask = mask;
+  return ok();
+}

@@ -1,0 +1,37 @@
+// launch.hpp -- internal (not exported) kernel launchers.  Arguments reaching
+// these functions have already been validated by the C ABI layer; each
+// launcher only chooses the grid and enqueues on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pab {
+
+// Sequence addressing shared by the fp32 kernel: sequence s = (outer, inner)
+// with outer = s / inner_count, inner = s % inner_count; its first query row
+// is q + outer*q_outer + inner*q_inner with consecutive rows q_row apart, and
+// likewise for keys/values.
+struct SeqLayout {
+  int64_t nseq;
+  int64_t inner_count;
+  int64_t q_outer, q_inner, q_row;
+  int64_t kv_outer, kv_inner, kv_row;
+  int64_t lq, lk;
+};
+
+hipError_t launch_spatial_bf16(const void* q, const void* k, const void* v, void* o, int64_t nseq,
+                               int S, int D, float scale, hipStream_t stream);
+hipError_t launch_temporal_bf16(const void* q, const void* k, const void* v, void* o, int64_t nbh,
+                                int F, int S, int D, float scale, hipStream_t stream);
+hipError_t launch_cross_bf16(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
+                             int64_t nq, int L, int D, float scale, hipStream_t stream);
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o,
+                           const SeqLayout& lay, int D, float scale, hipStream_t stream);
+
+int mse_num_blocks(int64_t n, int dtype);
+hipError_t launch_mse(const void* a, const void* b, int64_t n, int dtype, double* out,
+                      double* partials, hipStream_t stream);
+
+}  // namespace pab

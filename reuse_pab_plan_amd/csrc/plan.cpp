@@ -1,0 +1,56 @@
+// plan.cpp -- the broadcast schedule of Pyramid Attention Broadcast.
+//
+// PAB article, "Implementation": attention changes a lot in the first and
+// last 15% of the denoising steps and little in the middle 70%; in that
+// middle one step's attention output is broadcast to several following
+// steps, over a range chosen per attention type (wider for types that change
+// less; PAB abstract calls the set of ranges a pyramid).  Figure 2 caption:
+// at run time the broadcast output replaces the next few steps' attention.
+//
+// Integer arithmetic only, so the result is exact and platform-independent.
+// The window test is evaluated on i/N as 100*i against pct*N.
+#include <stdint.h>
+
+#include "abi.hpp"
+
+using namespace pab;
+
+extern "C" int pab_plan_schedule(int32_t num_steps, int32_t num_types, const int32_t* ranges,
+                                 int32_t window_lo_pct, int32_t window_hi_pct,
+                                 uint8_t* recompute, int32_t* source_step,
+                                 int32_t* recompute_count) {
+  if (num_steps < 1) return fail(PAB_ERR_INVALID_ARG, "pab_plan_schedule: num_steps must be >= 1");
+  if (num_types < 1 || num_types > 32)
+    return fail(PAB_ERR_INVALID_ARG, "pab_plan_schedule: num_types must be in [1, 32]");
+  if (!ranges || !recompute) return fail(PAB_ERR_INVALID_ARG, "pab_plan_schedule: NULL array");
+  if (!(0 <= window_lo_pct && window_lo_pct <= window_hi_pct && window_hi_pct <= 100))
+    return fail(PAB_ERR_INVALID_ARG, "pab_plan_schedule: need 0 <= lo <= hi <= 100");
+  for (int a = 0; a < num_types; ++a)
+    if (ranges[a] < 0) return fail(PAB_ERR_INVALID_ARG, "pab_plan_schedule: negative range");
+
+  const int64_t n = num_steps;
+  // First step of the stable window, and its length.
+  int64_t w0 = -1, w = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (100 * i >= (int64_t)window_lo_pct * n && 100 * i < (int64_t)window_hi_pct * n) {
+      if (w0 < 0) w0 = i;
+      ++w;
+    }
+  }
+  for (int a = 0; a < num_types; ++a) {
+    const int64_t period = (int64_t)ranges[a] + 1;
+    int32_t count = 0, src = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      const bool inside = w > 0 && i >= w0 && i < w0 + w;
+      const bool fresh = !inside || ((i - w0) % period) == 0;
+      if (fresh) {
+        src = (int32_t)i;
+        ++count;
+      }
+      recompute[i * num_types + a] = fresh ? 1 : 0;
+      if (source_step) source_step[i * num_types + a] = src;
+    }
+    if (recompute_count) recompute_count[a] = count;
+  }
+  return ok();
+}

@@ -1,0 +1,228 @@
+"""ctypes binding of libpab.so (declared in include/pab.h).
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name; all computation happens in the library's HIP kernels.
+Device tensors are torch tensors (torch provides device memory and streams).
+If the library is missing this module raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpab.so")
+
+PAB_OK = 0
+PAB_ERR_INVALID_ARG = -1
+PAB_ERR_UNSUPPORTED = -2
+PAB_ERR_DEVICE = -3
+PAB_ERR_CAPACITY = -4
+
+PAB_BF16 = 0
+PAB_F32 = 1
+
+PAB_SPATIAL = 0
+PAB_TEMPORAL = 1
+PAB_CROSS = 2
+KINDS = {"spatial": PAB_SPATIAL, "temporal": PAB_TEMPORAL, "cross": PAB_CROSS}
+
+# Every symbol include/pab.h declares.
+EXPORTED = (
+    "pab_plan_schedule",
+    "pab_attn_spatial",
+    "pab_attn_temporal",
+    "pab_attn_cross",
+    "pab_mse_workspace_bytes",
+    "pab_attn_diff_mse",
+    "pab_step_dispatch",
+    "pab_last_error",
+    "pab_version",
+)
+
+
+class PabError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class TypeDesc(C.Structure):
+    _fields_ = [
+        ("kind", C.c_int32),
+        ("q", C.c_void_p),
+        ("k", C.c_void_p),
+        ("v", C.c_void_p),
+        ("slot", C.c_void_p * 2),
+        ("B", C.c_int32),
+        ("H", C.c_int32),
+        ("F", C.c_int32),
+        ("S", C.c_int32),
+        ("D", C.c_int32),
+        ("L", C.c_int32),
+        ("drift", C.c_void_p),
+    ]
+
+
+class StepDesc(C.Structure):
+    _fields_ = [
+        ("num_steps", C.c_int32),
+        ("num_types", C.c_int32),
+        ("recompute", C.POINTER(C.c_uint8)),
+        ("types", C.POINTER(TypeDesc)),
+        ("dtype", C.c_int32),
+        ("softmax_scale", C.c_float),
+        ("workspace", C.c_void_p),
+        ("workspace_bytes", C.c_size_t),
+        ("stream", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Open libpab.so once and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m reuse_pab_plan_amd.build` "
+            "(the PAB path has no non-HIP fallback)"
+        )
+    lib = C.CDLL(path)
+    i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+    lib.pab_plan_schedule.argtypes = [i32, i32, C.POINTER(i32), i32, i32,
+                                      C.POINTER(C.c_uint8), C.POINTER(i32), C.POINTER(i32)]
+    lib.pab_plan_schedule.restype = C.c_int
+    for name in ("pab_attn_spatial", "pab_attn_temporal"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+        fn.restype = C.c_int
+    lib.pab_attn_cross.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp]
+    lib.pab_attn_cross.restype = C.c_int
+    lib.pab_mse_workspace_bytes.argtypes = [i64]
+    lib.pab_mse_workspace_bytes.restype = sz
+    lib.pab_attn_diff_mse.argtypes = [vp, vp, i64, i32, vp, vp, sz, vp]
+    lib.pab_attn_diff_mse.restype = C.c_int
+    lib.pab_step_dispatch.argtypes = [C.POINTER(StepDesc), i32, C.POINTER(C.c_uint32),
+                                      C.POINTER(C.c_void_p)]
+    lib.pab_step_dispatch.restype = C.c_int
+    lib.pab_last_error.argtypes = []
+    lib.pab_last_error.restype = C.c_char_p
+    lib.pab_version.argtypes = []
+    lib.pab_version.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != PAB_OK:
+        raise PabError(fn, status, load().pab_last_error().decode())
+
+
+def pab_last_error() -> str:
+    return load().pab_last_error().decode()
+
+
+def pab_version() -> str:
+    return load().pab_version().decode()
+
+
+# ------------------------------------------------------------------ host side
+
+def pab_plan_schedule(num_steps: int, ranges, window_lo_pct: int = 15, window_hi_pct: int = 85):
+    """Returns (recompute uint8 [N,T], source_step int32 [N,T], counts int32 [T])."""
+    lib = load()
+    t = len(ranges)
+    r = np.ascontiguousarray(np.asarray(ranges, dtype=np.int32))
+    rec = np.zeros((max(num_steps, 0), t), dtype=np.uint8)
+    src = np.zeros((max(num_steps, 0), t), dtype=np.int32)
+    cnt = np.zeros(t, dtype=np.int32)
+    st = lib.pab_plan_schedule(
+        num_steps, t, r.ctypes.data_as(C.POINTER(C.c_int32)), window_lo_pct, window_hi_pct,
+        rec.ctypes.data_as(C.POINTER(C.c_uint8)), src.ctypes.data_as(C.POINTER(C.c_int32)),
+        cnt.ctypes.data_as(C.POINTER(C.c_int32)),
+    )
+    _check("pab_plan_schedule", st)
+    return rec, src, cnt
+
+
+# ---------------------------------------------------------------- device side
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return PAB_BF16
+    if t.dtype == torch.float32:
+        return PAB_F32
+    raise PabError("binding", PAB_ERR_UNSUPPORTED, f"dtype {t.dtype} unsupported")
+
+
+def _stream_ptr(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr())
+
+
+def pab_attn_spatial(q, k, v, o, softmax_scale: float = 0.0, stream=None):
+    """q, k, v, o: [B, H, F, S, D] device tensors (bf16 or fp32)."""
+    B, H, F, S, D = q.shape
+    st = load().pab_attn_spatial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, F, S, D,
+                                 _dtype_code(q), softmax_scale, _stream_ptr(stream))
+    _check("pab_attn_spatial", st)
+    return o
+
+
+def pab_attn_temporal(q, k, v, o, softmax_scale: float = 0.0, stream=None):
+    """q, k, v, o: [B, H, F, S, D] device tensors (bf16 or fp32)."""
+    B, H, F, S, D = q.shape
+    st = load().pab_attn_temporal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, F, S, D,
+                                  _dtype_code(q), softmax_scale, _stream_ptr(stream))
+    _check("pab_attn_temporal", st)
+    return o
+
+
+def pab_attn_cross(q, k_text, v_text, o, softmax_scale: float = 0.0, stream=None):
+    """q, o: [B, H, ..., D] video queries; k_text, v_text: [B, H, L, D]."""
+    B, H = q.shape[0], q.shape[1]
+    D = q.shape[-1]
+    nq = q.numel() // (B * H * D)
+    L = k_text.shape[2]
+    st = load().pab_attn_cross(_ptr(q), _ptr(k_text), _ptr(v_text), _ptr(o), B, H, nq, L, D,
+                               _dtype_code(q), softmax_scale, _stream_ptr(stream))
+    _check("pab_attn_cross", st)
+    return o
+
+
+def pab_mse_workspace_bytes(n: int) -> int:
+    return int(load().pab_mse_workspace_bytes(n))
+
+
+def pab_attn_diff_mse(a, b, out, workspace, stream=None):
+    """out: 1-element float64 device tensor; workspace: device buffer (uint8)."""
+    n = a.numel()
+    st = load().pab_attn_diff_mse(_ptr(a), _ptr(b), n, _dtype_code(a), _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check("pab_attn_diff_mse", st)
+    return out
+
+
+def pab_step_dispatch(desc: StepDesc, step: int):
+    """Returns (recomputed_mask, [output pointer per type])."""
+    mask = C.c_uint32(0)
+    outs = (C.c_void_p * desc.num_types)()
+    st = load().pab_step_dispatch(C.byref(desc), step, C.byref(mask), outs)
+    _check("pab_step_dispatch", st)
+    return mask.value, [outs[a] for a in range(desc.num_types)]

@@ -1,0 +1,142 @@
+"""CPU-side tests of libpab.so: it loads, exports every declared symbol, the
+host planner is bit-exact against the oracle, and argument validation
+returns the documented codes before any device call (no kernels run here)."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import schedule as oracle_schedule
+from reuse_pab_plan_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pab.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH), reason="libpab.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pab_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = lib.load()
+    names = declared_functions()
+    assert set(names) == set(lib.EXPORTED)
+    for name in names:
+        assert hasattr(L, name), name
+    assert "gfx950" in lib.pab_version()
+
+
+@pytest.mark.parametrize("win", [(15, 85), (0, 100), (50, 50), (0, 0), (30, 60), (10, 90)])
+def test_planner_bit_exact_vs_oracle(win):
+    lo, hi = win
+    for n in list(range(1, 61)) + [97, 150, 200]:
+        for ranges in ([0], [2, 4, 6], [2, 3, 5], [1, 7], [12, 0, 3, 9]):
+            r1, s1, c1 = lib.pab_plan_schedule(n, ranges, lo, hi)
+            r2, s2, c2 = oracle_schedule(n, ranges, lo, hi)
+            assert np.array_equal(r1, r2), (n, ranges, win)
+            assert np.array_equal(s1, s2), (n, ranges, win)
+            assert np.array_equal(c1, c2), (n, ranges, win)
+
+
+def test_planner_config_counts():
+    # the three benchmark schedules
+    assert list(lib.pab_plan_schedule(10, [2, 3, 5])[2]) == [6, 5, 5]
+    assert list(lib.pab_plan_schedule(30, [2, 4, 6])[2]) == [16, 14, 12]
+    assert list(lib.pab_plan_schedule(50, [2, 6])[2]) == [27, 20]
+
+
+def test_planner_errors():
+    L = lib.load()
+    r = (C.c_int32 * 2)(1, 2)
+    rec = (C.c_uint8 * 20)()
+    assert L.pab_plan_schedule(0, 2, r, 15, 85, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_schedule(10, 0, r, 15, 85, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_schedule(10, 33, r, 15, 85, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_schedule(10, 2, None, 15, 85, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_schedule(10, 2, r, 60, 40, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_schedule(10, 2, r, -1, 40, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert "lo <= hi" in lib.pab_last_error()
+    neg = (C.c_int32 * 2)(1, -2)
+    assert L.pab_plan_schedule(10, 2, neg, 15, 85, rec, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_schedule(10, 2, r, 15, 85, rec, None, None) == lib.PAB_OK
+    assert lib.pab_last_error() == ""
+
+
+# Fake, never-dereferenced, 16-byte aligned addresses: validation must reject
+# every one of these calls before touching the device.
+A, B_, Cc, O = 0x10000, 0x20000000, 0x40000000, 0x60000000
+
+
+def test_attention_validation_codes():
+    L = lib.load()
+    sp = L.pab_attn_spatial
+    args = dict(B=1, H=2, F=3, S=5, D=64, dt=lib.PAB_BF16, sc=0.0)
+
+    def call(fn, q=A, k=B_, v=Cc, o=O, **kw):
+        a = {**args, **kw}
+        return fn(q, k, v, o, a["B"], a["H"], a["F"], a["S"], a["D"], a["dt"], a["sc"], None)
+
+    assert call(sp, q=None) == lib.PAB_ERR_INVALID_ARG
+    assert call(sp, q=A + 8) == lib.PAB_ERR_INVALID_ARG              # misaligned
+    assert call(sp, B=0) == lib.PAB_ERR_INVALID_ARG
+    assert call(sp, S=-4) == lib.PAB_ERR_INVALID_ARG
+    assert call(sp, D=60) == lib.PAB_ERR_UNSUPPORTED                 # not a multiple of 8
+    assert call(sp, D=136) == lib.PAB_ERR_UNSUPPORTED
+    assert call(sp, dt=7) == lib.PAB_ERR_UNSUPPORTED
+    assert call(sp, sc=-1.0) == lib.PAB_ERR_INVALID_ARG
+    assert call(sp, sc=float("nan")) == lib.PAB_ERR_INVALID_ARG
+    assert call(sp, o=A) == lib.PAB_ERR_INVALID_ARG                  # o aliases q
+    assert "overlap" in lib.pab_last_error()
+    assert call(L.pab_attn_temporal, F=65) == lib.PAB_ERR_UNSUPPORTED
+    cr = L.pab_attn_cross
+    assert cr(A, B_, Cc, O, 1, 2, 100, 129, 64, 0, 0.0, None) == lib.PAB_ERR_UNSUPPORTED  # L > 128
+    assert cr(A, B_, Cc, O, 1, 2, 0, 16, 64, 0, 0.0, None) == lib.PAB_ERR_INVALID_ARG
+    assert cr(A, B_, Cc, A, 1, 2, 100, 16, 64, 0, 0.0, None) == lib.PAB_ERR_INVALID_ARG
+
+
+def test_mse_validation_codes():
+    L = lib.load()
+    n = 1000
+    ws = lib.pab_mse_workspace_bytes(n)
+    assert ws >= 8 and ws % 256 == 0
+    assert lib.pab_mse_workspace_bytes(0) == 0
+    big = lib.pab_mse_workspace_bytes(10**9)
+    assert big >= 2048 * 8
+    assert L.pab_attn_diff_mse(A, B_, n, 0, O, Cc, ws - 8, None) == lib.PAB_ERR_CAPACITY
+    assert L.pab_attn_diff_mse(A, B_, 0, 0, O, Cc, ws, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_attn_diff_mse(A, B_, n, 3, O, Cc, ws, None) == lib.PAB_ERR_UNSUPPORTED
+    assert L.pab_attn_diff_mse(A + 4, B_, n, 0, O, Cc, ws, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_attn_diff_mse(A, B_, n, 0, O + 4, Cc, ws, None) == lib.PAB_ERR_INVALID_ARG
+
+
+def test_dispatch_validation_codes():
+    rec, _, _ = lib.pab_plan_schedule(4, [1])
+    t = lib.TypeDesc(kind=9, q=A, k=B_, v=Cc, B=1, H=1, F=1, S=8, D=64, L=0)
+    t.slot[0] = O
+    types = (lib.TypeDesc * 1)(t)
+    d = lib.StepDesc(num_steps=4, num_types=1,
+                     recompute=rec.ctypes.data_as(C.POINTER(C.c_uint8)),
+                     types=C.cast(types, C.POINTER(lib.TypeDesc)), dtype=0, softmax_scale=0.0)
+    L = lib.load()
+    assert L.pab_step_dispatch(C.byref(d), 0, None, None) == lib.PAB_ERR_INVALID_ARG  # bad kind
+    types[0].kind = lib.PAB_SPATIAL
+    assert L.pab_step_dispatch(C.byref(d), 4, None, None) == lib.PAB_ERR_INVALID_ARG  # step range
+    assert L.pab_step_dispatch(C.byref(d), -1, None, None) == lib.PAB_ERR_INVALID_ARG
+    types[0].D = 12
+    assert L.pab_step_dispatch(C.byref(d), 0, None, None) == lib.PAB_ERR_UNSUPPORTED
+    types[0].D = 64
+    types[0].slot[1] = O + 64   # overlapping second slot
+    assert L.pab_step_dispatch(C.byref(d), 0, None, None) == lib.PAB_ERR_INVALID_ARG
+    types[0].slot[1] = 0x70000000
+    types[0].drift = 0x78000000   # drift without a workspace
+    assert L.pab_step_dispatch(C.byref(d), 0, None, None) == lib.PAB_ERR_INVALID_ARG
+    d.workspace, d.workspace_bytes = 0x7c000000, 8
+    assert L.pab_step_dispatch(C.byref(d), 0, None, None) == lib.PAB_ERR_CAPACITY
+    assert L.pab_step_dispatch(None, 0, None, None) == lib.PAB_ERR_INVALID_ARG
