@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the PAB attention hot path on one MI355X.
+
+One benchmark step is one whole denoising trajectory of the 480p-latent DiT
+block (48 frames x 1590 tokens, 16 heads x 72, 120 text tokens, 30 steps,
+broadcast ranges spatial 2 / temporal 4 / cross 6, bf16): the schedule from
+pab_plan_schedule, then per step pab_step_dispatch for each attention type
+(spatial, temporal and cross kernels on recompute steps, nothing on
+broadcast steps) and the attention-difference MSE after every recompute.
+All inputs of the trajectory are generated into HBM before timing starts.
+
+Prints one JSON line: metric, value (attention TFLOP/s executed per second
+of PAB-on trajectory), ms_per_step (ms per PAB-on trajectory), the PAB-off
+trajectory beside it, per-kernel timings, the roofline of the dominant
+kernel (spatial attention, bf16 MFMA) measured live with HIP events on the
+launch stream, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config b480|b720|full3d|tiny]
+                    [--no-cpu-baseline] [--calib-copy]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and ms per denoise trajectory (PAB on/off), % of roofline"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_spatial_b480.json")
+KERNEL_SOURCES = {
+    "spatial": "reuse_pab_plan_amd/csrc/spatial.hip",
+    "temporal": "reuse_pab_plan_amd/csrc/temporal.hip",
+    "cross": "reuse_pab_plan_amd/csrc/cross.hip",
+    "mse": "reuse_pab_plan_amd/csrc/mse.hip",
+}
+
+
+def source_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed PAB-on trajectories")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--off-steps", type=int, default=5, help="timed PAB-off trajectories")
+    ap.add_argument("--config", default="b480")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def stats_ms(pairs):
+    import numpy as np
+
+    ms = np.array([a.elapsed_time(b) for a, b in pairs], dtype=np.float64)
+    if ms.size == 0:
+        return None
+    return {"n": int(ms.size), "mean_ms": float(ms.mean()), "median_ms": float(np.median(ms)),
+            "p10_ms": float(np.percentile(ms, 10)), "p90_ms": float(np.percentile(ms, 90))}
+
+
+def cpu_baseline(cfg, traj_on, inputs, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of the same workload.
+
+    Per attention type: oracle outputs for whole (b, h) slices of one
+    recompute step's inputs, adding heads until the type's share of the time
+    budget is used.  The oracle's trajectory time is derived as
+    sum_a count_a * flops_a / rate_a (every call of a type has the same shape).
+    """
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from reuse_pab_plan_amd import harness
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    per_type = budget_s / len(cfg.kinds)
+    rates, sample = [], []
+    step = 0
+    for a, kind in enumerate(cfg.kinds):
+        q, k, v = inputs.get(0, a, step)
+        done_flops, t_used, heads = 0, 0.0, 0
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                qh = q[b:b + 1, h:h + 1].float().cpu().numpy()
+                kh = k[b:b + 1, h:h + 1].float().cpu().numpy()
+                vh = v[b:b + 1, h:h + 1].float().cpu().numpy()
+                t0 = time.perf_counter()
+                if kind == "spatial":
+                    oracle.spatial(qh, kh, vh)
+                elif kind == "temporal":
+                    oracle.temporal(qh, kh, vh)
+                else:
+                    oracle.cross(qh, kh, vh)
+                t_used += time.perf_counter() - t0
+                heads += 1
+                done_flops += harness.attn_flops(cfg, kind) // (cfg.B * cfg.H)
+                if t_used >= per_type:
+                    break
+            if t_used >= per_type:
+                break
+        rates.append(done_flops / t_used)
+        sample.append(f"{kind}: {heads} of {cfg.B * cfg.H} (b,h) slices of one step")
+    traj_s = sum(int(traj_on.counts[a]) * harness.attn_flops(cfg, kind) * cfg.blocks / rates[a]
+                 for a, kind in enumerate(cfg.kinds))
+    value = traj_on.flops() / traj_s / 1e12
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "; ".join(sample) + f"; fp64 numpy oracle; trajectory time derived as "
+                  f"sum of count x per-call time = {traj_s:.1f} s per PAB-on trajectory",
+        "ms_per_trajectory": traj_s * 1e3,
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this PAB hot path has no multi-GPU mode "
+              "(sequence-parallel sharding is a design note, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from reuse_pab_plan_amd import harness, lib
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    lib.load()
+    cfg = harness.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+
+    traj_on = harness.Trajectory(cfg, pab=True, device=dev, stream=stream)
+    traj_off = harness.Trajectory(cfg, pab=False, device=dev, stream=stream)
+    t0 = time.time()
+    # PAB-off needs every step's inputs; PAB-on uses a subset of them.
+    inputs = harness.Inputs(cfg, traj_off.steps_needed(), device=dev, resident=True)
+    traj_on.inputs = inputs
+    traj_off.inputs = inputs
+    torch.cuda.synchronize()
+    log(f"config {cfg.name}: inputs generated in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB resident)")
+
+    if args.calib_copy:
+        # Plain copy of exactly 2 GiB read + 2 GiB written, for scaling the
+        # FETCH_SIZE / WRITE_SIZE counters of the attention kernels.
+        src = torch.empty(2**30, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for w in range(args.warmup):
+        traj_on.run(events=False)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    brackets = {"attn": [[] for _ in cfg.kinds], "mse": []}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        r = traj_on.run(events=True)
+        for a in range(len(cfg.kinds)):
+            brackets["attn"][a] += r["brackets"]["attn"][a]
+        brackets["mse"] += r["brackets"]["mse"]
+    stop.record(stream)
+    torch.cuda.synchronize()
+    on_ms = start.elapsed_time(stop) / args.steps
+    log(f"PAB on: {on_ms:.3f} ms per trajectory")
+
+    # Dispatch-mask check against the plan (bit-exact schedule in the timed runs).
+    for a in range(len(cfg.kinds)):
+        got = (r["masks"][0] >> a) & 1
+        if not (got == traj_on.recompute[:, a]).all():
+            raise RuntimeError(f"dispatch mask of type {a} differs from the schedule")
+
+    off_brackets = {"attn": [[] for _ in cfg.kinds], "mse": []}
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.off_steps):
+        r = traj_off.run(events=True)
+        for a in range(len(cfg.kinds)):
+            off_brackets["attn"][a] += r["brackets"]["attn"][a]
+    stop.record(stream)
+    torch.cuda.synchronize()
+    off_ms = start.elapsed_time(stop) / args.off_steps
+    log(f"PAB off: {off_ms:.3f} ms per trajectory")
+
+    kernels = {}
+    for a, kind in enumerate(cfg.kinds):
+        st = stats_ms(brackets["attn"][a])
+        flops = harness.attn_flops(cfg, kind)
+        by = harness.attn_bytes(cfg, kind)
+        st.update({
+            "launches_per_trajectory": int(traj_on.counts[a]) * cfg.blocks,
+            "flops_per_launch": flops,
+            "bytes_per_launch": by,
+            "tflops": flops / (st["mean_ms"] * 1e-3) / 1e12,
+            "gbs": by / (st["mean_ms"] * 1e-3) / 1e9,
+        })
+        if kind == "spatial":
+            st["frac_mfma"] = st["tflops"] / PEAK_BF16_TFLOPS
+        else:
+            st["frac_hbm"] = st["gbs"] / PEAK_HBM_GBS
+        kernels[kind] = st
+    st = stats_ms(brackets["mse"])
+    if st:
+        st.update({"bytes_per_launch": harness.mse_bytes(cfg),
+                   "gbs": harness.mse_bytes(cfg) / (st["mean_ms"] * 1e-3) / 1e9})
+        st["frac_hbm"] = st["gbs"] / PEAK_HBM_GBS
+        kernels["mse"] = st
+
+    flops_on = traj_on.flops()
+    flops_off = traj_off.flops()
+    value = flops_on / (on_ms * 1e-3) / 1e12
+
+    # Roofline of the dominant kernel (spatial attention: bf16 MFMA).
+    dom = "spatial"
+    ach = kernels[dom]["tflops"]
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("config") == cfg.name and tr.get("source_sha") == source_hash(KERNEL_SOURCES[dom]):
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": ach, "peak": peak,
+                "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
+                "kernel": f"spatial_kernel<{cfg.D}>",
+                "algorithmic_flops_per_launch": kernels[dom]["flops_per_launch"]}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": on_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.desc + ", broadcast ranges "
+                   + "/".join(f"{k} {r}" for k, r in zip(cfg.kinds, cfg.ranges))
+                   + ", PAB on; one step = one whole trajectory",
+                   "name": cfg.name, "blocks": cfg.blocks, "denoise_steps": cfg.N,
+                   "recomputes_per_type": dict(zip(cfg.kinds, map(int, traj_on.counts)))},
+        "pab_on_ms_per_trajectory": on_ms,
+        "pab_off_ms_per_trajectory": off_ms,
+        "pab_speedup": off_ms / on_ms,
+        "effective_tflops_vs_off_work": flops_off / (on_ms * 1e-3) / 1e12,
+        "pab_off_tflops": flops_off / (off_ms * 1e-3) / 1e12,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, traj_on, inputs, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

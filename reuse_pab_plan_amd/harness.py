@@ -1,0 +1,269 @@
+"""Trajectory harness: runs a denoising trajectory of one or more DiT blocks
+through libpab.so's broadcast schedule and step dispatcher.
+
+PAB article, Figure 2 caption: each step either computes an attention type or
+reuses the output broadcast from an earlier step.  The harness plans the
+schedule with ``pab_plan_schedule``, allocates the cache slots (two O-sized
+HBM buffers per block and type), and for every step calls
+``pab_step_dispatch`` once per attention type, bracketed by HIP events on the
+launch stream, followed on recompute steps by the attention-difference MSE
+between the new output and the one it replaces (PAB article, Figure 1
+caption).  torch supplies device memory, streams and events only.
+
+``CONFIGS`` holds the synthetic workloads, stand-ins for the video DiTs the
+pages measure (480p and 720p latent shapes, a 28-block stack, a full-3D
+attention model); their inputs come from ``synth``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+
+import numpy as np
+
+from . import lib, synth
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    dtype: str          # "bf16" or "f32"
+    B: int
+    H: int
+    F: int
+    S: int
+    D: int
+    L: int
+    N: int              # denoising steps
+    kinds: tuple        # attention types of one block
+    ranges: tuple       # broadcast range per type
+    blocks: int
+    seed: int
+    desc: str
+
+    @property
+    def video_shape(self):
+        return (self.B, self.H, self.F, self.S, self.D)
+
+    @property
+    def text_shape(self):
+        return (self.B, self.H, self.L, self.D)
+
+    @property
+    def elem_bytes(self):
+        return 2 if self.dtype == "bf16" else 4
+
+
+CONFIGS = {
+    "tiny": Config("tiny", "f32", 1, 4, 4, 64, 64, 16, 10, ("spatial", "temporal", "cross"),
+                   (2, 3, 5), 1, 1,
+                   "tiny fp32: 4 frames x 64 tokens, 4 heads x 64, 16 text tokens, 10 steps"),
+    "b480": Config("b480", "bf16", 1, 16, 48, 1590, 72, 120, 30, ("spatial", "temporal", "cross"),
+                   (2, 4, 6), 1, 2,
+                   "480p-latent block: 48 frames x 1590 tokens, 16 heads x 72, 120 text tokens, 30 steps"),
+    "b720": Config("b720", "bf16", 1, 16, 32, 3600, 72, 120, 30, ("spatial", "temporal", "cross"),
+                   (2, 4, 6), 1, 3,
+                   "720p-latent block: 32 frames x 3600 tokens, 16 heads x 72, 120 text tokens, 30 steps"),
+    "stack28": Config("stack28", "bf16", 1, 16, 48, 1590, 72, 120, 30,
+                      ("spatial", "temporal", "cross"), (2, 4, 6), 28, 4,
+                      "28-block stack at the 480p-latent shape, 30 steps"),
+    "full3d": Config("full3d", "bf16", 2, 24, 1, 16384, 64, 120, 50, ("spatial", "cross"), (2, 6),
+                     1, 5, "full-3D attention, CFG batch 2: 16384 tokens, 24 heads x 64, 120 text "
+                     "tokens, 50 steps"),
+}
+
+TYPE_INDEX = {"spatial": 0, "temporal": 1, "cross": 2}
+
+
+# ------------------------------------------------------------ algorithmic work
+
+def attn_flops(cfg: Config, kind: str) -> int:
+    """QK^T and PV multiply-adds (2 flops each) of one call; nothing padded."""
+    B, H, F, S, D, L = cfg.B, cfg.H, cfg.F, cfg.S, cfg.D, cfg.L
+    if kind == "spatial":
+        return 4 * B * H * F * S * S * D
+    if kind == "temporal":
+        return 4 * B * H * S * F * F * D
+    return 4 * B * H * F * S * L * D
+
+
+def attn_bytes(cfg: Config, kind: str) -> int:
+    """Compulsory HBM bytes of one call: inputs read once, output written once."""
+    n = cfg.B * cfg.H * cfg.F * cfg.S * cfg.D * cfg.elem_bytes
+    if kind == "cross":
+        return 2 * n + 2 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.elem_bytes
+    return 4 * n
+
+
+def mse_bytes(cfg: Config) -> int:
+    return 2 * cfg.B * cfg.H * cfg.F * cfg.S * cfg.D * cfg.elem_bytes
+
+
+# ------------------------------------------------------------------- inputs
+
+class Inputs:
+    """Per (block, type, step) Q/K/V device tensors.
+
+    resident=True generates every needed step up front (the timed region then
+    only reads HBM); otherwise tensors are generated on demand, outside the
+    timed brackets, into reusable buffers.
+    """
+
+    def __init__(self, cfg: Config, steps_needed, device="cuda", resident=True):
+        import torch
+
+        self.cfg, self.device, self.resident = cfg, device, resident
+        self.tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.store = {}
+        self.scratch = {}
+        if resident:
+            for (b, a, i) in steps_needed:
+                self.store[(b, a, i)] = self._make(b, a, i, None)
+
+    def _shapes(self, a):
+        kind = self.cfg.kinds[a]
+        kv = self.cfg.text_shape if kind == "cross" else self.cfg.video_shape
+        return self.cfg.video_shape, kv
+
+    def _make(self, b, a, i, out):
+        qs, kvs = self._shapes(a)
+        t = TYPE_INDEX[self.cfg.kinds[a]]
+        res = []
+        for tensor, shape in ((0, qs), (1, kvs), (2, kvs)):
+            dst = None if out is None else out[tensor]
+            res.append(synth.gpu_tensor(shape, self.cfg.seed, b, t, tensor, i, self.cfg.N,
+                                        self.cfg.dtype, self.device, out=dst))
+        return tuple(res)
+
+    def get(self, b, a, i):
+        if self.resident:
+            return self.store[(b, a, i)]
+        import torch
+
+        if a not in self.scratch:
+            qs, kvs = self._shapes(a)
+            self.scratch[a] = tuple(torch.empty(s, dtype=self.tdt, device=self.device)
+                                    for s in (qs, kvs, kvs))
+        return self._make(b, a, i, self.scratch[a])
+
+
+# --------------------------------------------------------------- trajectory
+
+class Trajectory:
+    """One PAB (or PAB-off) trajectory over ``cfg.blocks`` blocks."""
+
+    def __init__(self, cfg: Config, pab: bool = True, inputs: Inputs | None = None,
+                 device="cuda", drift: bool = True, stream=None):
+        import torch
+
+        self.cfg, self.pab, self.drift = cfg, pab, drift
+        self.device = torch.device(device)
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        ranges = list(cfg.ranges) if pab else [0] * len(cfg.kinds)
+        self.recompute, self.source, self.counts = lib.pab_plan_schedule(cfg.N, ranges)
+        self.T = len(cfg.kinds)
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        # Cache: two O-sized slots per (block, type), resident in HBM.
+        self.slots = [[(torch.empty(cfg.video_shape, dtype=tdt, device=self.device),
+                        torch.empty(cfg.video_shape, dtype=tdt, device=self.device))
+                       for _ in range(self.T)] for _ in range(cfg.blocks)]
+        n = int(np.prod(cfg.video_shape))
+        self.ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=self.device)
+        self.drift_out = torch.zeros((cfg.blocks, self.T, cfg.N), dtype=torch.float64,
+                                     device=self.device)
+        self.inputs = inputs
+        # One single-type step descriptor per (block, type), so each type's
+        # kernel can be bracketed by events of its own.
+        self._rec_cols = [np.ascontiguousarray(self.recompute[:, a]) for a in range(self.T)]
+        self._descs = []
+        self._types = []
+        for b in range(cfg.blocks):
+            row = []
+            for a in range(self.T):
+                t = (lib.TypeDesc * 1)()
+                t[0].kind = lib.KINDS[cfg.kinds[a]]
+                t[0].slot[0] = self.slots[b][a][0].data_ptr()
+                t[0].slot[1] = self.slots[b][a][1].data_ptr()
+                t[0].B, t[0].H, t[0].F, t[0].S, t[0].D = cfg.video_shape
+                t[0].L = cfg.L if cfg.kinds[a] == "cross" else 0
+                t[0].drift = None
+                d = lib.StepDesc(
+                    num_steps=cfg.N, num_types=1,
+                    recompute=self._rec_cols[a].ctypes.data_as(C.POINTER(C.c_uint8)),
+                    types=C.cast(t, C.POINTER(lib.TypeDesc)),
+                    dtype=lib.PAB_BF16 if cfg.dtype == "bf16" else lib.PAB_F32,
+                    softmax_scale=0.0, workspace=self.ws.data_ptr(),
+                    workspace_bytes=self.ws.numel(), stream=self.stream.cuda_stream)
+                row.append(d)
+                self._types.append(t)
+            self._descs.append(row)
+
+    def steps_needed(self):
+        return [(b, a, i) for b in range(self.cfg.blocks) for a in range(self.T)
+                for i in range(self.cfg.N) if self.recompute[i, a]]
+
+    def run(self, events: bool = False, on_step=None):
+        """Run the whole trajectory.  Returns a dict with the dispatch masks,
+        output pointers and (if events) per-type kernel and MSE brackets."""
+        import torch
+
+        cfg = self.cfg
+        masks = np.zeros((cfg.blocks, cfg.N), dtype=np.uint32)
+        outs = [[[None] * self.T for _ in range(cfg.N)] for _ in range(cfg.blocks)]
+        brackets = {"attn": [[] for _ in range(self.T)], "mse": []}
+        last = [[None] * self.T for _ in range(cfg.blocks)]
+        mk = (lambda: torch.cuda.Event(enable_timing=True)) if events else None
+        with torch.cuda.stream(self.stream):
+            for i in range(cfg.N):
+                for b in range(cfg.blocks):
+                    for a in range(self.T):
+                        d = self._descs[b][a]
+                        t = self._types[b * self.T + a]
+                        rec = bool(self.recompute[i, a])
+                        if rec:
+                            q, k, v = self.inputs.get(b, a, i)
+                            t[0].q, t[0].k, t[0].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+                        if events and rec:
+                            e0, e1 = mk(), mk()
+                            e0.record(self.stream)
+                        mask, ptrs = lib.pab_step_dispatch(d, i)
+                        if events and rec:
+                            e1.record(self.stream)
+                            brackets["attn"][a].append((e0, e1))
+                        masks[b, i] |= mask << a
+                        outs[b][i][a] = ptrs[0]
+                        if rec and self.drift and last[b][a] is not None:
+                            if events:
+                                m0, m1 = mk(), mk()
+                                m0.record(self.stream)
+                            self._mse(ptrs[0], last[b][a], self.drift_out[b, a, i])
+                            if events:
+                                m1.record(self.stream)
+                                brackets["mse"].append((m0, m1))
+                        if rec:
+                            last[b][a] = ptrs[0]
+                if on_step is not None:
+                    on_step(i, outs)
+        return {"masks": masks, "outs": outs, "brackets": brackets}
+
+    def _mse(self, a_ptr, b_ptr, out):
+        n = int(np.prod(self.cfg.video_shape))
+        st = lib.load().pab_attn_diff_mse(
+            C.c_void_p(a_ptr), C.c_void_p(b_ptr), n,
+            lib.PAB_BF16 if self.cfg.dtype == "bf16" else lib.PAB_F32,
+            C.c_void_p(out.data_ptr()), C.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+            C.c_void_p(self.stream.cuda_stream))
+        lib._check("pab_attn_diff_mse", st)
+
+    def slot_tensor(self, b, a, ptr):
+        """The cache slot tensor that lives at device address ``ptr``."""
+        for s in self.slots[b][a]:
+            if s.data_ptr() == ptr:
+                return s
+        raise KeyError(ptr)
+
+    def flops(self) -> int:
+        """Algorithmic attention flops this trajectory executes."""
+        return sum(int(self.counts[a]) * attn_flops(self.cfg, k) * self.cfg.blocks
+                   for a, k in enumerate(self.cfg.kinds))
