@@ -203,9 +203,10 @@ class Trajectory:
         return [(b, a, i) for b in range(self.cfg.blocks) for a in range(self.T)
                 for i in range(self.cfg.N) if self.recompute[i, a]]
 
-    def run(self, events: bool = False, on_step=None):
-        """Run the whole trajectory.  Returns a dict with the dispatch masks,
-        output pointers and (if events) per-type kernel and MSE brackets."""
+    def run(self, events: bool = False, on_step=None, max_steps=None):
+        """Run the trajectory (its first ``max_steps`` steps if given).
+        Returns a dict with the dispatch masks, output pointers and (if
+        events) per-type kernel and MSE brackets."""
         import torch
 
         cfg = self.cfg
@@ -215,7 +216,7 @@ class Trajectory:
         last = [[None] * self.T for _ in range(cfg.blocks)]
         mk = (lambda: torch.cuda.Event(enable_timing=True)) if events else None
         with torch.cuda.stream(self.stream):
-            for i in range(cfg.N):
+            for i in range(cfg.N if max_steps is None else min(max_steps, cfg.N)):
                 for b in range(cfg.blocks):
                     for a in range(self.T):
                         d = self._descs[b][a]

@@ -1,0 +1,184 @@
+"""GPU tests of the broadcast cache and step dispatch through the C ABI.
+
+Over whole trajectories: the dispatch mask equals the oracle's schedule at
+every step (bit-exact); at every broadcast step the output is the very slot
+written at the source step, with bitwise-identical bytes; recomputed outputs
+match the oracle (sampled at full size); the drift MSE the dispatcher
+computes equals the oracle MSE of the two outputs; PAB off recomputes every
+step.  PAB article, Figure 2 caption (broadcast to the next few steps) and
+Figure 1 caption (difference between steps measured by the MSE).
+"""
+
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reuse_pab_plan_amd import harness, lib
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.load()
+
+
+def _fingerprint(t):
+    """Exact content fingerprint of a device tensor (int64 sums of the bits)."""
+    bits = t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    x = bits.to(torch.int64).flatten()
+    idx = torch.arange(x.numel(), device=x.device, dtype=torch.int64)
+    return (int(x.sum()), int((x * (idx % 65521 + 1)).sum()))
+
+
+def _sample_check(cfg, kind, q, k, v, out, label):
+    B, H, F, S, D = cfg.video_shape
+    host = lambda t: t.detach().float().cpu().numpy()
+    if kind == "spatial":
+        sl = (slice(B - 1, B), slice(H - 1, H), slice(F - 1, F))
+        rows = np.arange(0, S, max(1, S // 200))
+        ref = oracle.spatial_rows(host(q[sl]), host(k[sl]), host(v[sl]), 0, 0, 0, rows)
+        got = host(out[B - 1, H - 1, F - 1])[rows]
+    elif kind == "temporal":
+        pos = np.arange(0, S, max(1, S // 50))
+        ref = oracle.temporal_positions(host(q[0, 0][None, None]), host(k[0, 0][None, None]),
+                                        host(v[0, 0][None, None]), 0, 0, pos)
+        got = host(out[0, 0])[:, pos]
+    else:
+        nq = F * S
+        rows = np.arange(0, nq, max(1, nq // 1000))
+        ref = oracle.cross_rows(host(q.view(B, H, nq, D)[0, 1][None, None]),
+                                host(k[0, 1][None, None]), host(v[0, 1][None, None]), 0, 0, rows)
+        got = host(out.view(B, H, nq, D)[0, 1])[rows]
+    err = got - ref
+    mx, rl = float(np.abs(err).max()), float(np.linalg.norm(err) / np.linalg.norm(ref))
+    tol = (2e-2, 5e-3) if cfg.dtype == "bf16" else (1e-5, 1e-5)
+    print(f"[parity] {label}: max_abs={mx:.2e} rel_l2={rl:.2e}", flush=True)
+    assert mx <= tol[0] and rl <= tol[1], (label, mx, rl)
+
+
+def _run_checked(cfg, pab=True, blocks_checked=(0,), check_steps=None, resident=True,
+                 max_steps=None):
+    dev = torch.device("cuda:0")
+    traj = harness.Trajectory(cfg, pab=pab, device=dev)
+    need = traj.steps_needed()
+    if max_steps is not None:
+        need = [x for x in need if x[2] < max_steps]
+    traj.inputs = harness.Inputs(cfg, need, device=dev, resident=resident)
+    ranges = list(cfg.ranges) if pab else [0] * len(cfg.kinds)
+    rec, src, cnt = oracle.schedule(cfg.N, ranges)
+    assert np.array_equal(traj.recompute, rec) and np.array_equal(traj.counts, cnt)
+    prints = {}
+    w0 = -(-15 * cfg.N // 100)
+    check_steps = set(check_steps if check_steps is not None else (0, w0, cfg.N - 1))
+
+    def on_step(i, outs):
+        torch.cuda.synchronize()
+        for b in blocks_checked:
+            for a, kind in enumerate(cfg.kinds):
+                ptr = outs[b][i][a]
+                slot = traj.slot_tensor(b, a, ptr)
+                j = int(src[i, a])
+                if j == i:
+                    prints[(b, a, i)] = _fingerprint(slot)
+                    if i in check_steps:
+                        q, k, v = traj.inputs.get(b, a, i)
+                        _sample_check(cfg, kind, q, k, v, slot, f"{cfg.name} b{b} {kind} step {i}")
+                else:
+                    assert ptr == outs[b][j][a], "reuse must hand back the source slot"
+                    assert _fingerprint(slot) == prints[(b, a, j)], "reused bytes changed"
+
+    res = traj.run(on_step=on_step, max_steps=max_steps)
+    n = cfg.N if max_steps is None else max_steps
+    for b in range(cfg.blocks):
+        for i in range(n):
+            for a in range(len(cfg.kinds)):
+                assert ((int(res["masks"][b, i]) >> a) & 1) == rec[i, a]
+    return traj, res
+
+
+def test_tiny_trajectory_every_step():
+    _need_gpu()
+    cfg = harness.CONFIGS["tiny"]
+    _run_checked(cfg, check_steps=range(cfg.N))
+
+
+def test_tiny_trajectory_pab_off():
+    _need_gpu()
+    cfg = harness.CONFIGS["tiny"]
+    traj, res = _run_checked(cfg, pab=False, check_steps=(0, 5, 9))
+    assert (traj.counts == cfg.N).all()
+
+
+def test_b480_trajectory():
+    _need_gpu()
+    _run_checked(harness.CONFIGS["b480"])
+
+
+def test_full3d_trajectory():
+    _need_gpu()
+    _run_checked(harness.CONFIGS["full3d"], check_steps=(8,))
+
+
+def test_stack28_cache_first_steps():
+    # 28 blocks x 3 types x 2 slots resident in HBM; the first 8 steps cover
+    # the outer steps, the window entry (step 5) and broadcast steps 6, 7.
+    _need_gpu()
+    cfg = harness.CONFIGS["stack28"]
+    _run_checked(cfg, blocks_checked=(0, 13, 27), check_steps=(5,), resident=False, max_steps=8)
+
+
+def test_drift_matches_oracle_mse():
+    # PAB off: consecutive-step attention differences (the Figure 1 analogue),
+    # computed on the device by the dispatcher's own two-slot drift path.
+    _need_gpu()
+    cfg = harness.Config("drift", "bf16", 1, 2, 4, 96, 72, 40, 10,
+                         ("spatial", "temporal", "cross"), (0, 0, 0), 1, 12, "drift")
+    dev = torch.device("cuda:0")
+    rec, _, _ = lib.pab_plan_schedule(cfg.N, [0, 0, 0])
+    inputs = harness.Inputs(cfg, [(0, a, i) for a in range(3) for i in range(cfg.N)], device=dev)
+    slots = [(torch.empty(cfg.video_shape, dtype=torch.bfloat16, device=dev),
+              torch.empty(cfg.video_shape, dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+    drift = torch.full((3, cfg.N), -1.0, dtype=torch.float64, device=dev)
+    n = int(np.prod(cfg.video_shape))
+    ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    types = (lib.TypeDesc * 3)()
+    for a, kind in enumerate(cfg.kinds):
+        types[a].kind = lib.KINDS[kind]
+        types[a].slot[0] = slots[a][0].data_ptr()
+        types[a].slot[1] = slots[a][1].data_ptr()
+        types[a].B, types[a].H, types[a].F, types[a].S, types[a].D = cfg.video_shape
+        types[a].L = cfg.L
+        types[a].drift = drift[a].data_ptr()
+    stream = torch.cuda.current_stream()
+    desc = lib.StepDesc(num_steps=cfg.N, num_types=3,
+                        recompute=rec.ctypes.data_as(C.POINTER(C.c_uint8)),
+                        types=C.cast(types, C.POINTER(lib.TypeDesc)), dtype=lib.PAB_BF16,
+                        softmax_scale=0.0, workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
+                        stream=stream.cuda_stream)
+    prev = [None] * 3
+    expect = np.full((3, cfg.N), -1.0)
+    for i in range(cfg.N):
+        for a in range(3):
+            q, k, v = inputs.get(0, a, i)
+            types[a].q, types[a].k, types[a].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+        mask, outs = lib.pab_step_dispatch(desc, i)
+        assert mask == 0b111
+        torch.cuda.synchronize()
+        for a in range(3):
+            cur = [s for s in slots[a] if s.data_ptr() == outs[a]][0]
+            host = cur.float().cpu().numpy()
+            if prev[a] is not None:
+                expect[a, i] = oracle.mse(host, prev[a])
+            prev[a] = host
+    got = drift.cpu().numpy()
+    assert (got[:, 0] == -1.0).all()  # no predecessor: left untouched
+    rel = np.abs(got[:, 1:] - expect[:, 1:]) / expect[:, 1:]
+    print(f"[parity] drift max rel err {rel.max():.2e}", flush=True)
+    assert rel.max() <= 1e-6
+    # The synthetic workload's U shape: outer steps differ more than inner ones.
+    assert got[:, 1].min() > 10 * got[:, 4:8].max()
