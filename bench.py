@@ -35,7 +35,7 @@ METRIC = "attention TFLOP/s and ms per denoise trajectory (PAB on/off), % of roo
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_spatial_b480.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_b480.md")
 KERNEL_SOURCES = {
     "spatial": "reuse_pab_plan_amd/csrc/spatial.hip",
     "temporal": "reuse_pab_plan_amd/csrc/temporal.hip",
@@ -47,6 +47,23 @@ KERNEL_SOURCES = {
 def source_hash(rel):
     with open(os.path.join(ROOT, rel), "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def read_traffic(config, kernel):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    tr = json.loads(text[start + 7:end])
+    k = tr.get("kernels", {}).get(kernel)
+    if tr.get("config") != config or not k or k.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -161,7 +178,8 @@ def main():
     traj_off = harness.Trajectory(cfg, pab=False, device=dev, stream=stream)
     t0 = time.time()
     # PAB-off needs every step's inputs; PAB-on uses a subset of them.
-    inputs = harness.Inputs(cfg, traj_off.steps_needed(), device=dev, resident=True)
+    needed = traj_off.steps_needed() if args.off_steps > 0 else traj_on.steps_needed()
+    inputs = harness.Inputs(cfg, needed, device=dev, resident=True)
     traj_on.inputs = inputs
     traj_off.inputs = inputs
     torch.cuda.synchronize()
@@ -203,17 +221,16 @@ def main():
         if not (got == traj_on.recompute[:, a]).all():
             raise RuntimeError(f"dispatch mask of type {a} differs from the schedule")
 
-    off_brackets = {"attn": [[] for _ in cfg.kinds], "mse": []}
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.off_steps):
-        r = traj_off.run(events=True)
-        for a in range(len(cfg.kinds)):
-            off_brackets["attn"][a] += r["brackets"]["attn"][a]
-    stop.record(stream)
-    torch.cuda.synchronize()
-    off_ms = start.elapsed_time(stop) / args.off_steps
-    log(f"PAB off: {off_ms:.3f} ms per trajectory")
+    off_ms = None
+    if args.off_steps > 0:
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(args.off_steps):
+            traj_off.run(events=False)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        off_ms = start.elapsed_time(stop) / args.off_steps
+        log(f"PAB off: {off_ms:.3f} ms per trajectory")
 
     kernels = {}
     for a, kind in enumerate(cfg.kinds):
@@ -231,12 +248,14 @@ def main():
             st["frac_mfma"] = st["tflops"] / PEAK_BF16_TFLOPS
         else:
             st["frac_hbm"] = st["gbs"] / PEAK_HBM_GBS
+        st["traffic"] = read_traffic(cfg.name, kind)
         kernels[kind] = st
     st = stats_ms(brackets["mse"])
     if st:
         st.update({"bytes_per_launch": harness.mse_bytes(cfg),
                    "gbs": harness.mse_bytes(cfg) / (st["mean_ms"] * 1e-3) / 1e9})
         st["frac_hbm"] = st["gbs"] / PEAK_HBM_GBS
+        st["traffic"] = read_traffic(cfg.name, "mse")
         kernels["mse"] = st
 
     flops_on = traj_on.flops()
@@ -247,12 +266,7 @@ def main():
     dom = "spatial"
     ach = kernels[dom]["tflops"]
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as fh:
-            tr = json.load(fh)
-        if tr.get("config") == cfg.name and tr.get("source_sha") == source_hash(KERNEL_SOURCES[dom]):
-            traffic = tr.get("bytes_per_launch")
+    traffic = read_traffic(cfg.name, dom)
     roofline = {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": ach, "peak": peak,
                 "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
                 "kernel": f"spatial_kernel<{cfg.D}>",
@@ -278,9 +292,9 @@ def main():
                    "recomputes_per_type": dict(zip(cfg.kinds, map(int, traj_on.counts)))},
         "pab_on_ms_per_trajectory": on_ms,
         "pab_off_ms_per_trajectory": off_ms,
-        "pab_speedup": off_ms / on_ms,
+        "pab_speedup": (off_ms / on_ms) if off_ms else None,
         "effective_tflops_vs_off_work": flops_off / (on_ms * 1e-3) / 1e12,
-        "pab_off_tflops": flops_off / (off_ms * 1e-3) / 1e12,
+        "pab_off_tflops": (flops_off / (off_ms * 1e-3) / 1e12) if off_ms else None,
         "kernels": kernels,
         "roofline": roofline,
     }
