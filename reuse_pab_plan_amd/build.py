@@ -56,6 +56,8 @@ def _compile(src: str) -> tuple[str, float, str]:
         line for line in (res.stdout + res.stderr).splitlines()
         if "packed-fp32-ops" not in line  # host pass does not know the device feature
     )
+    if "warning:" not in out and "error" not in out:
+        out = ""
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{out}")
     return obj, time.time() - t0, out

@@ -75,4 +75,22 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 // Lane exchange with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// v_permlane32_swap of a value with itself: .lo holds, in every lane, the value
+// of the lower half-wave lane of the same column (lane % 32), .y that of the
+// upper half-wave lane (.hi).
+struct HalfPair {
+  float lo, hi;
+};
+__device__ __forceinline__ HalfPair half_pair(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+
+// Max over the two half-wave lanes that share a column.
+__device__ __forceinline__ float max_halves(float v) {
+  const HalfPair p = half_pair(v);
+  return fmaxf(p.lo, p.hi);
+}
+
 }  // namespace pab

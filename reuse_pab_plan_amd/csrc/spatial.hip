@@ -4,12 +4,13 @@
 //
 // Per sequence (b, h, f) of S tokens: O = softmax(Q K^T * scale) V.
 //
-// Work split: a 256-thread block owns 256 query rows of one sequence, 64 per
-// wave (two 32-row MFMA blocks, so every K and V operand read from LDS feeds
-// two MFMAs).  The block sweeps the sequence's keys in tiles of 64 staged
-// row-major in LDS (double-buffered; the next tile's loads are in flight in
-// registers while the current tile computes).  Each 64-key tile is consumed
-// as two 32-key blocks:
+// Work split: a 256-thread block owns up to 256 query rows of one sequence,
+// 64 per wave (two 32-row MFMA blocks, so every K and V operand read from LDS
+// feeds two MFMAs; one block per wave for heads wider than 88).  Keys arrive
+// in 64-row tiles through a 3-stage LDS ring filled by direct global->LDS
+// loads (global_load_lds_dwordx4) issued two tiles ahead, so the next tiles
+// stream in while the current one computes and no registers are spent on
+// staging.  Each tile is consumed as two 32-key blocks:
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of
 //     ONE query row, so row statistics need one exchange with the other
 //     half-wave;
@@ -17,9 +18,10 @@
 //     block's max exceeds it by more than 8 (log2 units); p <= 2^8 and
 //     rescales become rare after the first blocks;
 //   * O^T += V^T P^T: the V^T operand comes straight from the row-major V
-//     tile through ds_read_b64_tr_b16 (transposing LDS read), and an implicit
-//     all-ones row D of V^T makes the MFMA produce sum_j p_ij (the softmax
-//     denominator, over exactly the bf16-rounded p that multiply V).
+//     tile through ds_read_b64_tr_b16 (transposing LDS read).  Operand row D
+//     (a padding row of the last 32-row block) is set to ones, so O^T row D
+//     accumulates sum_j p_ij -- the softmax denominator, over exactly the
+//     bf16-rounded p that multiply V -- on the MFMA.
 // Blocks are remapped so that the query tiles of one sequence share an XCD
 // (and its L2), where the sequence's K and V stay resident.
 #include "device.hpp"
@@ -32,11 +34,28 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBN = 64;                  // keys per LDS tile
+constexpr int kStages = 3;               // LDS ring depth (loads run two tiles ahead)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;           // lazy-rescale threshold (log2 units)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Smallest row stride (elements, multiple of 8, >= min_elems) whose first four
+// rows start on disjoint 8-bank spans: the transposing read of one 16-lane
+// group touches 32 bytes of four consecutive rows.
+constexpr int tr_stride(int min_elems) {
+  for (int s = (min_elems + 7) / 8 * 8;; s += 8) {
+    const int w = s / 2;  // 4-byte words per row
+    bool ok = true;
+    for (int a = 0; a < 4 && ok; ++a)
+      for (int b = a + 1; b < 4 && ok; ++b) {
+        const int d = (w * (b - a)) % 64;
+        if (d < 8 || d > 56) ok = false;
+      }
+    if (ok) return s;
+  }
+}
 
 template <int D>
 struct Geo {
@@ -46,33 +65,65 @@ struct Geo {
   static constexpr int BM = kWaves * 32 * QB;       // query rows per block
   static constexpr int ND = (D + 15) / 16;          // 16-wide d steps of Q K^T
   static constexpr int NB = D / 32 + 1;             // 32-row blocks of O^T (rows 0..D)
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  // Even chunk counts put rows on repeating bank patterns; rotate each row's
-  // chunks by ((row % 32) >> 1) so the 32 rows an MFMA operand read touches
-  // spread over the banks.  Odd counts (e.g. D = 72) are conflict-free as
-  // they are.
-  static constexpr bool ROT = (CPR % 2) == 0;
-  static constexpr int TILE_CHUNKS = kBN * CPR;      // per tensor per tile
-  static constexpr int LOADS = (TILE_CHUNKS + kThreads - 1) / kThreads;
-  // A stage holds one K (or V) tile.  Every thread moves LOADS chunks per
-  // tile unconditionally; chunks past the tile land in the slack behind it,
-  // which also absorbs the d over-read of the last key row when D % 16 == 8.
-  static constexpr int TILE_ELEMS = (LOADS * kThreads + CPR) * 8 + 32;
+  static constexpr int DCH = D / 8;                 // 16-byte chunks of data per row
+  // K rows: an odd number of 16-byte chunks keeps the 32 rows of one MFMA
+  // operand read on distinct banks.
+  static constexpr int KS = (DCH % 2) ? D : D + 8;
+  static constexpr int KCH = KS / 8;
+  // V rows: data padded to a stride that keeps the transposing reads
+  // conflict-free.
+  static constexpr int VS = tr_stride(D);
+  static constexpr int VCH = VS / 8;
+  // Direct loads per thread per tile, rounded up; surplus slots land in the
+  // stage's tail (which also absorbs the operand over-reads past row 63).
+  static constexpr int KDMA = (kBN * KCH + kThreads - 1) / kThreads;
+  static constexpr int VDMA = (kBN * VCH + kThreads - 1) / kThreads;
+  static constexpr int KSTAGE = KDMA * kThreads * 8;  // elements
+  static constexpr int VSTAGE = VDMA * kThreads * 8;
+  // The last 32-row O^T block holds row D (the denominator); with no data in
+  // it (D % 32 == 0) its V^T operand is a constant and is not read.
+  static constexpr bool LAST_READ = (NB - 1) * 32 < D;
+  // Transposing reads of V past the last data column (operand rows > D, whose
+  // products are discarded) may run past the stage's slots into this slack.
+  static constexpr int VSLACK = 64;
+  static constexpr int STAGE = KSTAGE + VSTAGE + VSLACK;
+  // K over-reads (d >= D, multiplied by Q's zero padding) must hit finite
+  // data: they stay inside the DMA'd slots, surplus slots included.
+  static_assert(kBN * KS + 8 <= KSTAGE, "K over-read must stay in the DMA'd slots");
+  static_assert((kBN - 1) * VS + (LAST_READ ? NB : NB - 1) * 32 <= VSTAGE + VSLACK,
+                "V over-read must stay in the stage");
+  static_assert(kStages * STAGE * 2 <= 160 * 1024, "LDS ring too large");
+  static_assert(KDMA + VDMA < 32, "vmcnt budget");
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
 };
 
-template <int D>
-__device__ __forceinline__ int phys_chunk(int row, int ch) {
-  using G = Geo<D>;
-  if constexpr (G::ROT) {
-    int p = ch + ((row & 31) >> 1);
-    p %= G::CPR;
-    return p;
-  } else {
-    return ch;
-  }
+// One 16-byte direct global->LDS load per lane: lane l of the wave reads
+// global bytes [gbase + voff, +16) and writes LDS bytes [lds + 16*l, +16).
+// `gbase` and `lds` must be wave-uniform.  Issued from inline assembly so that
+// the wait for it (s_waitcnt vmcnt) is placed by hand: the compiler would
+// otherwise wait for every outstanding direct load before each LDS read,
+// serializing the ring.  The instruction has no result register.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// Keeps the compiler from hoisting address arithmetic on `x` out of a loop
+// (it would otherwise spend one VGPR and two adds per distinct LDS offset).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 template <int D>
@@ -82,11 +133,11 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
                                                              bf16* __restrict__ O, int S, int nqt,
                                                              int nblocks, float c) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][G::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 vs[2][G::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 ring[kStages * G::STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int logical = xcd_remap(blockIdx.x, nblocks);
   const int64_t seq = logical / nqt;
   const int qt = logical % nqt;
@@ -96,13 +147,7 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   const bf16* __restrict__ Vs = V + base;
   bf16* __restrict__ Os = O + base;
 
-  // Slack after each K tile must be finite (read by the d over-read, times 0).
-  if (tid < 32) {
-    ks[0][kBN * D + tid] = (bf16)0.f;
-    ks[1][kBN * D + tid] = (bf16)0.f;
-  }
-
-  // This wave's 64 query rows as the B operand (Q^T), resident in registers.
+  // This wave's query rows as the B operand (Q^T), resident in registers.
   const int qrow0 = qt * G::BM + wave * 32 * G::QB;
   const bool wave_live = qrow0 < S;
   bf16x8 qreg[G::QB][G::ND];
@@ -117,80 +162,70 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
                          : zero_bf16x8();
     }
   }
+  // Let Q land before the ring starts: the compiler tracks these loads but
+  // not the direct loads, and would otherwise wait for everything in flight
+  // at the first use of Q inside the loop.
+  wait_vmcnt<0>();
 
-  // Global -> register staging of one tile (K and V, 16-byte chunks).  Rows
-  // past S load row S-1 instead: finite values whose scores are masked.
-  // Chunk slots past the tile load a valid chunk and land in the stage's
-  // slack, so no lane needs a branch.
-  // (Named variables, not arrays: an array indexed across the loop would be
-  // placed in scratch memory.)
-  int go0 = 0, go1 = 0, go2 = 0, go3 = 0, so0 = 0, so1 = 0, so2 = 0, so3 = 0;
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-  static_assert(G::LOADS <= 4, "staging holds at most 4 chunks per thread");
-#define PAB_OFFS(I, go, so)                                                   \
-  if constexpr (G::LOADS > I) {                                               \
-    const int cidx = tid + I * kThreads;                                      \
-    const int row = cidx / G::CPR, ch = cidx % G::CPR;                        \
-    go = cidx < G::TILE_CHUNKS ? row * D + ch * 8 : 0;                        \
-    so = row * D + phys_chunk<D>(row, ch) * 8;                                \
+  // Direct-load plan of this thread: slot s = i*256 + tid of the K (V) stage
+  // holds chunk (row, ch) = (s / KCH, s % KCH) of the tile.  Pad chunks
+  // (ch >= D/8) and surplus slots re-read chunk 0 of the tile: finite values
+  // that nothing uses.  Byte offsets are relative to the tile's first row.
+  uint32_t koff[G::KDMA], voff[G::VDMA];
+#pragma unroll
+  for (int i = 0; i < G::KDMA; ++i) {
+    const int s = i * kThreads + tid, row = s / G::KCH, ch = s % G::KCH;
+    koff[i] = (row < kBN && ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
   }
-  PAB_OFFS(0, go0, so0) PAB_OFFS(1, go1, so1) PAB_OFFS(2, go2, so2) PAB_OFFS(3, go3, so3)
-#undef PAB_OFFS
-#define PAB_FETCH_ONE(I, go, kx, vx)                                          \
-  if constexpr (G::LOADS > I) {                                               \
-    const int row_ = go / D;                                                  \
-    const int shift_ = key0_ + row_ < S ? key0_ * D : (S - 1 - row_) * D;     \
-    kx = *reinterpret_cast<const uint4*>(Ks + (size_t)(go + shift_));         \
-    vx = *reinterpret_cast<const uint4*>(Vs + (size_t)(go + shift_));         \
+#pragma unroll
+  for (int i = 0; i < G::VDMA; ++i) {
+    const int s = i * kThreads + tid, row = s / G::VCH, ch = s % G::VCH;
+    voff[i] = (row < kBN && ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
   }
-#define PAB_FETCH(t)                                                          \
-  do {                                                                        \
-    const int key0_ = (t) * kBN;                                              \
-    PAB_FETCH_ONE(0, go0, k0, v0) PAB_FETCH_ONE(1, go1, k1, v1)               \
-    PAB_FETCH_ONE(2, go2, k2, v2) PAB_FETCH_ONE(3, go3, k3, v3)               \
-  } while (0)
-#define PAB_STASH_ONE(I, so, kx, vx)                                          \
-  if constexpr (G::LOADS > I) {                                               \
-    *reinterpret_cast<uint4*>(&ks[buf_][so]) = kx;                            \
-    *reinterpret_cast<uint4*>(&vs[buf_][so]) = vx;                            \
-  }
-#define PAB_STASH(buf)                                                        \
-  do {                                                                        \
-    const int buf_ = (buf);                                                   \
-    PAB_STASH_ONE(0, so0, k0, v0) PAB_STASH_ONE(1, so1, k1, v1)               \
-    PAB_STASH_ONE(2, so2, k2, v2) PAB_STASH_ONE(3, so3, k3, v3)               \
-  } while (0)
-
-  // Per-lane LDS offsets (elements) of the K operand reads, per (kb, ds).
-  int koff[2][G::ND];
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)LDS_PTR(void, ring);
+  const uint32_t wave_slot = (uint32_t)(wave * kWave * 16);
+  auto issue = [&](int t) {
+    const int key0 = t * kBN;
+    const uint32_t st = ring_lds + (uint32_t)((t % kStages) * G::STAGE * 2) + wave_slot;
+    if (key0 + kBN <= S) {
+      const bf16* kt = Ks + (size_t)key0 * D;
+      const bf16* vt = Vs + (size_t)key0 * D;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < G::KDMA; ++i) dma16(kt, koff[i], st + (uint32_t)(i * kThreads * 16));
 #pragma unroll
-    for (int ds = 0; ds < G::ND; ++ds) {
-      const int row = kb * 32 + l32, ch = ds * 2 + h;
-      koff[kb][ds] = row * D + (ch < G::CPR ? phys_chunk<D>(row, ch) * 8 : ch * 8);
-    }
-  // Per-lane LDS offsets of the transposing V reads, per (t2 of a 32-key
-  // block, nb, first/second 4-key group); the key block adds kb*32 rows.
-  // Lane j of a 16-lane group addresses row (j/4) and columns 4*(j%4)..+3 of
-  // a 4x16 block and receives column j: the V^T operand row d = l32.
-  const int g16 = lane >> 4, j16 = lane & 15;
-  int voff[2][G::NB][2];
-  bool vread[G::NB];
+      for (int i = 0; i < G::VDMA; ++i)
+        dma16(vt, voff[i], st + (uint32_t)(G::KSTAGE * 2 + i * kThreads * 16));
+    } else {
+      // Ragged last tile: rows past S repeat row S-1 (finite; their scores
+      // are masked and their p are 0).
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) vread[nb] = nb * 32 < D;
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int row = t2 * 16 + half * 8 + h * 4 + (j16 >> 2);
-        const int col = nb * 32 + (g16 & 1) * 16 + (j16 & 3) * 4;
-        const int ch = col / 8;
-        voff[t2][nb][half] =
-            row * D + (col < D ? phys_chunk<D>(row, ch) * 8 + (col & 7) : 0);
+      for (int i = 0; i < G::KDMA; ++i) {
+        const int s = i * kThreads + tid, row = s / G::KCH, ch = s % G::KCH;
+        const int r = min(key0 + min(row, kBN - 1), S - 1);
+        const uint32_t off = (row < kBN && ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
+        dma16(Ks, off, st + (uint32_t)(i * kThreads * 16));
       }
+#pragma unroll
+      for (int i = 0; i < G::VDMA; ++i) {
+        const int s = i * kThreads + tid, row = s / G::VCH, ch = s % G::VCH;
+        const int r = min(key0 + min(row, kBN - 1), S - 1);
+        const uint32_t off = (row < kBN && ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
+        dma16(Vs, off, st + (uint32_t)(G::KSTAGE * 2 + i * kThreads * 16));
+      }
+    }
+  };
+
+  // Per-lane LDS bases of the operand reads; the rest of each address is a
+  // compile-time offset.  Transposing V read: lane j of a 16-lane group
+  // addresses row j/4 and columns 4*(j%4)..+3 of a 4x16 block and receives
+  // column j, i.e. V^T row d = l32 of the operand.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const uint32_t klane = (uint32_t)((l32 * G::KS + h * 8) * 2);
+  const uint32_t vlane =
+      (uint32_t)(((h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 + (j16 & 3) * 4) * 2);
+  // Operand row D of V^T (the ones row) lives in lane D % 32 of block D / 32.
+  const bool ones_lane = l32 == (D % 32);
+  const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
 
   f32x16 oacc[G::QB][G::NB];
 #pragma unroll
@@ -202,16 +237,22 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   for (int qb = 0; qb < G::QB; ++qb) mrow[qb] = -INFINITY;  // log2 domain (score * c)
 
   const int nt = (S + kBN - 1) / kBN;
-  PAB_FETCH(0);
-  PAB_STASH(0);
-  __syncthreads();
+  issue(0);
+  if (nt > 1) issue(1);
 
   for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) PAB_FETCH(t + 1);
+    // Tile t has landed once at most one tile's loads are still in flight.
+    if (t + 1 < nt) {
+      wait_vmcnt<G::KDMA + G::VDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (t + 2 < nt) issue(t + 2);  // refills the stage read in iteration t-1
     if (wave_live) {
-      const bf16* kb_ = ks[buf];
-      const bf16* vb = vs[buf];
+      const uint32_t stage = ring_lds + (uint32_t)((t % kStages) * G::STAGE * 2);
+      const uint32_t kaddr = opaque(stage + klane);
+      const uint32_t vaddr = opaque(stage + (uint32_t)(G::KSTAGE * 2) + vlane);
       const int key0 = t * kBN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -220,7 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
         for (int qb = 0; qb < G::QB; ++qb) sacc[qb] = zero16();
 #pragma unroll
         for (int ds = 0; ds < G::ND; ++ds) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_ + koff[kb][ds]);
+          const bf16x8 a =
+              *LDS_PTR(const bf16x8, kaddr + (uint32_t)((kb * 32 * G::KS + ds * 16) * 2));
 #pragma unroll
           for (int qb = 0; qb < G::QB; ++qb) sacc[qb] = mfma32(a, qreg[qb][ds], sacc[qb]);
         }
@@ -237,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
           float mx = sacc[qb][0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-          mx = fmaxf(mx, xor32(mx));
+          mx = max_halves(mx);
           const float mnew = mx * c;
           if (mnew > mrow[qb] + kSlack) {
             const float alpha = fast_exp2(mrow[qb] - mnew);
@@ -263,25 +305,22 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
 #pragma unroll
           for (int nb = 0; nb < G::NB; ++nb) {
             bf16x8 a;
-            const int d = nb * 32 + l32;
-            if (vread[nb]) {
-              const bf16* vrow = vb + kb * 32 * D;
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  LDS_PTR(i16x4, vrow + voff[t2][nb][0]));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  LDS_PTR(i16x4, vrow + voff[t2][nb][1]));
+            if (nb < G::NB - 1 || G::LAST_READ) {
+              const uint32_t p = vaddr + (uint32_t)(((kb * 32 + t2 * 16) * G::VS + nb * 32) * 2);
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+              const i16x4 hi =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
               a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-              if ((nb + 1) * 32 > D) {  // block holds d >= D: ones row D, zeros above
-                const bf16 fill = (bf16)(d == D ? 1.f : 0.f);
-                if (d >= D) {
-#pragma unroll
-                  for (int j = 0; j < 8; ++j) a[j] = fill;
-                }
+              if (nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
+                uint4 w = __builtin_bit_cast(uint4, a);
+                w.x = ones_lane ? ones_word : w.x;
+                w.y = ones_lane ? ones_word : w.y;
+                w.z = ones_lane ? ones_word : w.z;
+                w.w = ones_lane ? ones_word : w.w;
+                a = __builtin_bit_cast(bf16x8, w);
               }
             } else {
-              const bf16 fill = (bf16)(d == D ? 1.f : 0.f);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) a[j] = fill;
+              a = __builtin_bit_cast(bf16x8, make_uint4(ones_word, ones_word, ones_word, ones_word));
             }
 #pragma unroll
             for (int qb = 0; qb < G::QB; ++qb) oacc[qb][nb] = mfma32(a, pb[qb][t2], oacc[qb][nb]);
@@ -289,20 +328,13 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
         }
       }
     }
-    if (t + 1 < nt) PAB_STASH(buf ^ 1);
-    __syncthreads();
   }
 
-#undef PAB_FETCH
-#undef PAB_FETCH_ONE
-#undef PAB_STASH
-#undef PAB_STASH_ONE
   if (wave_live) {
 #pragma unroll
     for (int qb = 0; qb < G::QB; ++qb) {
-      const float own = oacc[qb][G::NBD][G::RD];
-      const float other = xor32(own);
-      const float inv = 1.f / ((h == G::HD) ? own : other);
+      const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
+      const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
       const int qrow = qrow0 + qb * 32 + l32;
       if (qrow < S) {
         bf16* orow = Os + (size_t)qrow * D;
