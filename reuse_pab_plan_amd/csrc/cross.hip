@@ -3,14 +3,23 @@
 // the text to the video and changes least between steps).
 //
 // Per (b, h): the Nq = F*S video queries against L <= 128 text keys.  The
-// text K (row-major) and V (transposed, plus an all-ones row at index D that
-// makes the MFMA emit the softmax denominator) are loaded into LDS once per
-// block and stay resident; query tiles of 32 rows stream from HBM through
-// each wave, so Q is read once and O written once: the kernel is HBM-bound.
-// Scores are formed transposed (S^T = K Q^T, v_mfma_f32_32x32x16_bf16) so
-// one lane holds one query row's scores; with at most 128 keys the whole row
-// fits in registers and the softmax needs no running rescale.  The next
-// tile's Q is loaded while the current tile computes.
+// text K and V (row-major, read with 16-byte vector loads) are loaded into LDS
+// once per block and stay resident; 32-row query tiles stream from HBM
+// through each wave, so Q is read once and O written once: the kernel is
+// HBM-bound.
+//   * Scores are formed transposed (S^T = K Q^T, v_mfma_f32_32x32x16_bf16) so
+//     one lane holds one query row's scores; with at most 128 keys the whole
+//     row fits in registers and the softmax needs no running max.
+//   * When D is not a multiple of 16 the Q K^T contraction is padded anyway;
+//     the padding column d = D carries a key bias (0 for real keys, -1e30 for
+//     the padding keys past L) against a 1 in Q, so padding keys are masked
+//     by the MFMA itself.
+//   * The V^T operand comes from the row-major V through ds_read_b64_tr_b16,
+//     with its padding row D set to ones so the MFMA emits the softmax
+//     denominator.
+//   * Q of the tile two ahead is loaded while the current one computes
+//     (non-temporal: each byte is read once); each wave's output tile is
+//     staged in LDS and written with lane-contiguous 16-byte stores.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -20,181 +29,290 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kLMax = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Smallest row stride (elements, multiple of 8, >= min_elems) whose first four
+// rows start on disjoint 8-bank spans (one 16-lane group of a transposing read
+// touches 32 bytes of four consecutive rows).
+constexpr int tr_stride(int min_elems) {
+  for (int s = (min_elems + 7) / 8 * 8;; s += 8) {
+    const int w = s / 2;
+    bool ok = true;
+    for (int a = 0; a < 4 && ok; ++a)
+      for (int b = a + 1; b < 4 && ok; ++b) {
+        const int d = (w * (b - a)) % 64;
+        if (d < 8 || d > 56) ok = false;
+      }
+    if (ok) return s;
+  }
+}
+
+// Row stride (elements) with an odd number of 16-byte chunks, >= min_elems:
+// the 32 rows read by one MFMA operand load then sit on distinct banks.
+constexpr int odd_chunk_stride(int min_elems) {
+  const int s = (min_elems + 7) / 8 * 8;
+  return ((s / 8) % 2) ? s : s + 8;
+}
+
+template <int D, int NKB>
 struct Geo {
-  static constexpr int ND = (D + 15) / 16;
-  static constexpr int NB = D / 32 + 1;
-  static constexpr int KS = ((D / 8) % 2 == 1) ? D : D + 8;
-  static constexpr int KROWS = kLMax + 1;
-  static constexpr int VS = kLMax + 4;
-  static constexpr int VROWS = NB * 32;
-  static constexpr int CPR = D / 8;
+  static constexpr int ND = (D + 15) / 16;             // 16-wide d steps of Q K^T
+  static constexpr int NB = D / 32 + 1;                // 32-row blocks of O^T
+  static constexpr bool BIAS = (D % 16) != 0;          // padding column d = D exists
+  static constexpr int KS = odd_chunk_stride(BIAS ? D + 8 : D);
+  static constexpr int KROWS = NKB * 32 + 1;           // +1: keeps row reads in bounds
+  static constexpr int VS = tr_stride(D);
+  static constexpr int VROWS = NKB * 32;
+  static constexpr int VSLACK = 64;                    // transposing over-read past the last row
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per input row
+  static constexpr bool LAST_READ = (NB - 1) * 32 < D;
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
 };
 
-template <int D>
-__device__ __forceinline__ void load_q(bf16x8 (&qr)[Geo<D>::ND], const bf16* __restrict__ Qh,
-                                       int64_t tile, int64_t nq, int l32, int h) {
-  const int64_t row = tile * 32 + l32;
-#pragma unroll
-  for (int ds = 0; ds < Geo<D>::ND; ++ds) {
-    const int d0 = ds * 16 + h * 8;
-    qr[ds] = (row < nq && d0 < D) ? *reinterpret_cast<const bf16x8*>(Qh + row * D + d0) : zero_bf16x8();
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void cross_kernel(const bf16* __restrict__ Q,
-                                                        const bf16* __restrict__ Kt,
-                                                        const bf16* __restrict__ Vt,
-                                                        bf16* __restrict__ O, int64_t nq, int L,
-                                                        int tiles_per_block, int blocks_per_bh,
-                                                        int nblocks, float c) {
-  using G = Geo<D>;
+template <int D, int NKB>
+__global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restrict__ Q,
+                                                           const bf16* __restrict__ Kt,
+                                                           const bf16* __restrict__ Vt,
+                                                           bf16* __restrict__ O, int64_t nq, int L,
+                                                           int tiles_per_block, int blocks_per_bh,
+                                                           int nblocks, float c) {
+  using G = Geo<D, NKB>;
   __shared__ __attribute__((aligned(16))) bf16 ks[G::KROWS * G::KS];
-  __shared__ __attribute__((aligned(16))) bf16 vt[G::VROWS * G::VS];
+  __shared__ __attribute__((aligned(16))) bf16 vs[G::VROWS * G::VS + G::VSLACK];
+  // Per-wave output tile (32 rows x D, row-major).
+  __shared__ __attribute__((aligned(16))) bf16 ostage[kWaves][32 * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int logical = xcd_remap(blockIdx.x, nblocks);
-  const int64_t bh = logical / blocks_per_bh;
+  const int bh = logical / blocks_per_bh;
   const int chunk = logical % blocks_per_bh;
-  const bf16* __restrict__ Qh = Q + bh * nq * D;
-  bf16* __restrict__ Oh = O + bh * nq * D;
-  const bf16* __restrict__ Kh = Kt + bh * (int64_t)L * D;
-  const bf16* __restrict__ Vh = Vt + bh * (int64_t)L * D;
+  const bf16* __restrict__ Qh = Q + (int64_t)bh * nq * D;
+  bf16* __restrict__ Oh = O + (int64_t)bh * nq * D;
+  const bf16* __restrict__ Kh = Kt + (int64_t)bh * L * D;
+  const bf16* __restrict__ Vh = Vt + (int64_t)bh * L * D;
 
-  const int64_t ntiles = (nq + 31) / 32;
-  const int64_t t_begin = (int64_t)chunk * tiles_per_block;
-  int64_t t_end = t_begin + tiles_per_block;
-  if (t_end > ntiles) t_end = ntiles;
+  const int ntiles = (int)((nq + 31) / 32);
+  const int t_begin = chunk * tiles_per_block;
+  const int t_end = min(t_begin + tiles_per_block, ntiles);
 
-  // Text K -> LDS rows (rows >= L and the pad row are zero).
-  for (int i = tid; i < G::KROWS * G::CPR; i += kThreads) {
-    const int row = i / G::CPR, ch = i % G::CPR;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (row < L) val = *reinterpret_cast<const uint4*>(Kh + (int64_t)row * D + ch * 8);
-    *reinterpret_cast<uint4*>(&ks[row * G::KS + ch * 8]) = val;
-  }
-  // Text V -> V^T in LDS; row D = 1 (denominator), rows > D and keys >= L = 0.
-  for (int i = tid; i < G::VROWS * kLMax; i += kThreads) {
-    const int d = i / kLMax, key = i % kLMax;
-    float val = 0.f;
-    if (d < D) {
-      if (key < L) val = (float)Vh[(int64_t)key * D + d];
-    } else if (d == D) {
-      val = 1.f;
+  // Text K and V -> LDS, row-major, 16-byte vectors; all loads of a thread
+  // are issued before its stores.  Rows >= L: K zero, V zero (their p are 0).
+  {
+    constexpr int kChunks = G::KROWS * G::CPR;
+    constexpr int kIter = (kChunks + kThreads - 1) / kThreads;
+    uint4 kr[kIter], vr[kIter];
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+      const int i = tid + it * kThreads;
+      const int row = i / G::CPR, ch = i % G::CPR;
+      const bool valid = i < kChunks && row < L;
+      const int64_t g = valid ? (int64_t)row * D + ch * 8 : 0;
+      kr[it] = valid ? *reinterpret_cast<const uint4*>(Kh + g) : make_uint4(0u, 0u, 0u, 0u);
+      vr[it] = valid ? *reinterpret_cast<const uint4*>(Vh + g) : make_uint4(0u, 0u, 0u, 0u);
     }
-    vt[d * G::VS + key] = (bf16)val;
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+      const int i = tid + it * kThreads;
+      const int row = i / G::CPR, ch = i % G::CPR;
+      if (i < kChunks) {
+        *reinterpret_cast<uint4*>(&ks[row * G::KS + ch * 8]) = kr[it];
+        if (row < G::VROWS) *reinterpret_cast<uint4*>(&vs[row * G::VS + ch * 8]) = vr[it];
+      }
+    }
+    // Columns D..KS-1 of every K row: the key bias at d = D (when it exists),
+    // zeros after it.
+    for (int i = tid; i < G::KROWS; i += kThreads) {
+#pragma unroll
+      for (int d = D; d < G::KS; ++d) {
+        float val = 0.f;
+        if (G::BIAS && d == D && i >= L) val = -1e30f;
+        ks[i * G::KS + d] = (bf16)val;
+      }
+    }
   }
   __syncthreads();
 
-  const int nkb = (L + 31) / 32;
-  bf16x8 qcur[G::ND], qnext[G::ND];
-  int64_t tile = t_begin + wave;
-  if (tile < t_end) load_q<D>(qcur, Qh, tile, nq, l32, h);
+  // Transposing V read: lane j of a 16-lane group addresses row j/4, columns
+  // 4*(j%4)..+3 of a 4x16 block and receives column j (operand row d = l32).
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const uint32_t vs_lds = (uint32_t)(uintptr_t)LDS_PTR(void, vs);
+  const uint32_t vlane =
+      vs_lds + (uint32_t)(((h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 + (j16 & 3) * 4) * 2);
+  const uint32_t ks_lds = (uint32_t)(uintptr_t)LDS_PTR(void, ks);
+  const uint32_t klane = ks_lds + (uint32_t)((l32 * G::KS + h * 8) * 2);
+  const bool ones_lane = l32 == (D % 32);
+  const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
+  // Q padding word at d = D (1 in its low half) when the bias column is used.
+  const uint32_t qpad_word = G::BIAS ? 0x00003F80u : 0u;
 
-  for (; tile < t_end; tile += kWaves) {
-    if (tile + kWaves < t_end) load_q<D>(qnext, Qh, tile + kWaves, nq, l32, h);
-
-    f32x16 sacc[4];
+  // Q tile (B operand, Q^T) as 32-bit words: lane (row l32, half h) holds
+  // d = ds*16 + h*8 .. +7 for each d step.
+  auto load_q = [&](u32x4 (&qr)[G::ND], int tile) {
+    const int64_t row = (int64_t)tile * 32 + l32;
+    const bool live = row < nq;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = zero16();
-      if (kb < nkb) {
-#pragma unroll
-        for (int ds = 0; ds < G::ND; ++ds) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&ks[(kb * 32 + l32) * G::KS + ds * 16 + h * 8]);
-          sacc[kb] = mfma32(a, qcur[ds], sacc[kb]);
-        }
+    for (int ds = 0; ds < G::ND; ++ds) {
+      const int d0 = ds * 16 + h * 8;
+      if (ds * 16 + 8 < D) {  // both halves hold data
+        qr[ds] = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Qh + row * D + d0))
+                      : u32x4{0u, 0u, 0u, 0u};
+      } else {  // last step of a D % 16 == 8 head: the upper half is padding
+        const u32x4 pad = {qpad_word, 0u, 0u, 0u};
+        qr[ds] = (h == 0 && live)
+                     ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Qh + row * D + d0))
+                     : (h == 0 ? u32x4{0u, 0u, 0u, 0u} : pad);
       }
     }
-    float mx = -INFINITY;
+  };
+
+  // One 32-row query tile against the text keys: full-row softmax,
+  // O = P V / sum(P) on the MFMA, row-major staging, coalesced stores.
+  bf16* ost = ostage[wave];
+  auto compute = [&](const u32x4 (&q)[G::ND], int tile) {
+    f32x16 sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kb * 32 + acc_row(r, h) >= L) sacc[kb][r] = -INFINITY;
-        mx = fmaxf(mx, sacc[kb][r]);
+      for (int ds = 0; ds < G::ND; ++ds) {
+        const u32x4 a = *LDS_PTR(const u32x4, klane + (uint32_t)((kb * 32 * G::KS + ds * 16) * 2));
+        sacc[kb] = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, q[ds]), sacc[kb]);
       }
-    mx = fmaxf(mx, xor32(mx));
+    }
+    if (!G::BIAS && (L & 31)) {  // ragged key end without a bias column
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((NKB - 1) * 32 + acc_row(r, h) >= L) sacc[NKB - 1][r] = -INFINITY;
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = max_halves(mx);
     const float negm = -mx * c;
 
     f32x16 oacc[G::NB];
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = zero16();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb < nkb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int r0 = t2 * 8;
-          const bf16x8 pb = to_bf16x8(
-              fast_exp2(fmaf(sacc[kb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 1], c, negm)),
-              fast_exp2(fmaf(sacc[kb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 3], c, negm)),
-              fast_exp2(fmaf(sacc[kb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 5], c, negm)),
-              fast_exp2(fmaf(sacc[kb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 7], c, negm)));
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int r0 = t2 * 8;
+        const bf16x8 pb = to_bf16x8(
+            fast_exp2(fmaf(sacc[kb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 1], c, negm)),
+            fast_exp2(fmaf(sacc[kb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 3], c, negm)),
+            fast_exp2(fmaf(sacc[kb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 5], c, negm)),
+            fast_exp2(fmaf(sacc[kb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 7], c, negm)));
 #pragma unroll
-          for (int nb = 0; nb < G::NB; ++nb) {
-            const bf16* row = &vt[(nb * 32 + l32) * G::VS + kb * 32 + t2 * 16 + h * 4];
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[nb] = mfma32(a, pb, oacc[nb]);
+        for (int nb = 0; nb < G::NB; ++nb) {
+          u32x4 a;
+          if (nb < G::NB - 1 || G::LAST_READ) {
+            const uint32_t p = vlane + (uint32_t)(((kb * 32 + t2 * 16) * G::VS + nb * 32) * 2);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            a = u32x4{l2.x, l2.y, h2.x, h2.y};
+            if (nb == G::NB - 1) {  // operand rows > D are don't-care; row D is ones
+              a.x = ones_lane ? ones_word : a.x;
+              a.y = ones_lane ? ones_word : a.y;
+              a.z = ones_lane ? ones_word : a.z;
+              a.w = ones_lane ? ones_word : a.w;
+            }
+          } else {
+            a = u32x4{ones_word, ones_word, ones_word, ones_word};
           }
+          oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, a), pb, oacc[nb]);
         }
       }
     }
 
-    const float own = oacc[G::NBD][G::RD];
-    const float other = xor32(own);
-    const float inv = 1.f / ((h == G::HD) ? own : other);
-    const int64_t row = tile * 32 + l32;
-    if (row < nq) {
-      bf16* orow = Oh + row * D;
+    const HalfPair pr = half_pair(oacc[G::NBD][G::RD]);
+    const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+    // Accumulators -> row-major tile in LDS (lane: row l32, 4 d per piece).
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
+    for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g) {
+        if (nb * 32 + g * 8 < D) {  // d0 = nb*32 + g*8 + h*4 < D (D % 8 == 0)
           const int d0 = nb * 32 + g * 8 + h * 4;
-          if (d0 < D) {
-            const uint2 w = make_uint2(pack_bf16x2(oacc[nb][g * 4 + 0] * inv, oacc[nb][g * 4 + 1] * inv),
-                                       pack_bf16x2(oacc[nb][g * 4 + 2] * inv, oacc[nb][g * 4 + 3] * inv));
-            *reinterpret_cast<uint2*>(orow + d0) = w;
-          }
+          const uint2 w = make_uint2(pack_bf16x2(oacc[nb][g * 4 + 0] * inv, oacc[nb][g * 4 + 1] * inv),
+                                     pack_bf16x2(oacc[nb][g * 4 + 2] * inv, oacc[nb][g * 4 + 3] * inv));
+          *reinterpret_cast<uint2*>(&ost[l32 * D + d0]) = w;
         }
-    }
+      }
+    __builtin_amdgcn_wave_barrier();
+    // Tile rows are contiguous in HBM: copy out 1 KB per instruction.
+    constexpr int kOutChunks = 32 * D / 8;
+    const int64_t rows_left = nq - (int64_t)tile * 32;
+    const int valid_chunks = rows_left >= 32 ? kOutChunks : (int)rows_left * (D / 8);
+    bf16* obase = Oh + (int64_t)tile * 32 * D;
 #pragma unroll
-    for (int ds = 0; ds < G::ND; ++ds) qcur[ds] = qnext[ds];
+    for (int i = 0; i < (kOutChunks + kWave - 1) / kWave; ++i) {
+      const int ch = i * kWave + lane;
+      if (ch < valid_chunks)
+        *reinterpret_cast<uint4*>(obase + ch * 8) = *reinterpret_cast<const uint4*>(&ost[ch * 8]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // This wave's tiles: t_begin + wave, + 4, + 8, ...  Q of the tile two
+  // ahead is loaded while the current one computes (three register sets).
+  u32x4 qa[G::ND], qb[G::ND], qc[G::ND];
+  int tile = t_begin + wave;
+  constexpr int step = kWaves;
+  if (tile < t_end) load_q(qa, tile);
+  if (tile + step < t_end) load_q(qb, tile + step);
+  for (; tile < t_end; tile += 3 * step) {
+    if (tile + 2 * step < t_end) load_q(qc, tile + 2 * step);
+    compute(qa, tile);
+    if (tile + step >= t_end) break;
+    if (tile + 3 * step < t_end) load_q(qa, tile + 3 * step);
+    compute(qb, tile + step);
+    if (tile + 2 * step >= t_end) break;
+    if (tile + 4 * step < t_end) load_q(qb, tile + 4 * step);
+    compute(qc, tile + 2 * step);
   }
 }
 
-template <int D>
-hipError_t launch_d(const void* q, const void* kt, const void* vt, void* o, int64_t nbh, int64_t nq,
-                    int L, float c, hipStream_t stream) {
-  // Size the grid to whole waves of resident blocks (3 per CU on 256 CUs),
-  // with at most 48 query tiles per block.
+template <int D, int NKB>
+hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
+                     int64_t nq, int L, float c, hipStream_t stream) {
+  // Size the grid to whole waves of resident blocks (2 per CU on 256 CUs),
+  // with at most 96 query tiles per block (the K/V load is amortized over
+  // them).
   const int64_t ntiles = (nq + 31) / 32;
   const int64_t total = ntiles * nbh;
-  const int64_t wave_blocks = 768;
-  int64_t target = ((total + wave_blocks * 48 - 1) / (wave_blocks * 48)) * wave_blocks;
+  const int64_t wave_blocks = 512;
+  int64_t target = ((total + wave_blocks * 96 - 1) / (wave_blocks * 96)) * wave_blocks;
   int64_t blocks_per_bh = (target + nbh - 1) / nbh;
   if (blocks_per_bh > ntiles) blocks_per_bh = ntiles;
   if (blocks_per_bh < 1) blocks_per_bh = 1;
   const int64_t tiles_per_block = (ntiles + blocks_per_bh - 1) / blocks_per_bh;
   blocks_per_bh = (ntiles + tiles_per_block - 1) / tiles_per_block;
   const int64_t nblocks = blocks_per_bh * nbh;
-  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(cross_kernel<D>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+  if (nblocks > 0x7fffffff || ntiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((cross_kernel<D, NKB>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)kt, (const bf16*)vt, (bf16*)o, nq, L,
                      (int)tiles_per_block, (int)blocks_per_bh, (int)nblocks, c);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* kt, const void* vt, void* o, int64_t nbh, int64_t nq,
+                    int L, float c, hipStream_t stream) {
+  if (L <= 32) return launch_dk<D, 1>(q, kt, vt, o, nbh, nq, L, c, stream);
+  if (L <= 64) return launch_dk<D, 2>(q, kt, vt, o, nbh, nq, L, c, stream);
+  return launch_dk<D, 4>(q, kt, vt, o, nbh, nq, L, c, stream);
 }
 
 }  // namespace
