@@ -113,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
                          : zero_bf16x8();
     }
   __syncthreads();
-  if (!live) return;
 
+  if (live) {
   const bf16* kp = ks + (size_t)pos * F * G::KS;
   const bf16* vp = vs + (size_t)pos * F * G::KS;
   const int nsteps = (F + 15) / 16;   // 16-frame PV steps
@@ -138,67 +138,96 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
     return a;
   };
 
+  // Phase 1: probabilities of both 32-frame query blocks.  All reads of K
+  // happen here, before any output is staged in the K rows.
+  bf16x8 pbs[2][4];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    if (qb >= nqb) break;
-    f32x16 sacc[2];
+    if (qb < nqb) {
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = zero16();
-      if (kb < nqb) {
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = zero16();
+        if (kb < nqb) {
 #pragma unroll
-        for (int ds = 0; ds < G::ND; ++ds) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + (size_t)(kb * 32 + l32) * G::KS +
-                                                            ds * 16 + h * 8);
-          sacc[kb] = mfma32(a, qreg[qb][ds], sacc[kb]);
+          for (int ds = 0; ds < G::ND; ++ds) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + (size_t)(kb * 32 + l32) * G::KS +
+                                                              ds * 16 + h * 8);
+            sacc[kb] = mfma32(a, qreg[qb][ds], sacc[kb]);
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (kb * 32 + acc_row(r, h) >= F) sacc[kb][r] = -INFINITY;
+          mx = fmaxf(mx, sacc[kb][r]);
+        }
+      mx = max_halves(mx);
+      const float negm = -mx * c;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < nsteps) {
+          const int kb = t >> 1, r0 = (t & 1) * 8;
+          pbs[qb][t] = to_bf16x8(
+              fast_exp2(fmaf(sacc[kb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 1], c, negm)),
+              fast_exp2(fmaf(sacc[kb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 3], c, negm)),
+              fast_exp2(fmaf(sacc[kb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 5], c, negm)),
+              fast_exp2(fmaf(sacc[kb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 7], c, negm)));
         }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kb * 32 + acc_row(r, h) >= F) sacc[kb][r] = -INFINITY;
-        mx = fmaxf(mx, sacc[kb][r]);
-      }
-    mx = fmaxf(mx, xor32(mx));
-    const float negm = -mx * c;
+  }
 
+  // Phase 2: O^T = V^T P^T per query block, then staged row-major in LDS.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (qb >= nqb) break;
     f32x16 oacc[G::NB];
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = zero16();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t < nsteps) {
-        const int kb = t >> 1, r0 = (t & 1) * 8;
-        const bf16x8 pb = to_bf16x8(
-            fast_exp2(fmaf(sacc[kb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 1], c, negm)),
-            fast_exp2(fmaf(sacc[kb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 3], c, negm)),
-            fast_exp2(fmaf(sacc[kb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 5], c, negm)),
-            fast_exp2(fmaf(sacc[kb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 7], c, negm)));
 #pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = mfma32(v_operand(nb, t), pb, oacc[nb]);
+        for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = mfma32(v_operand(nb, t), pbs[qb][t], oacc[nb]);
       }
     }
 
-    const float own = oacc[G::NBD][G::RD];
-    const float other = xor32(own);
-    const float inv = 1.f / ((h == G::HD) ? own : other);
+    const HalfPair pr = half_pair(oacc[G::NBD][G::RD]);
+    const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
     const int frame = qb * 32 + l32;
+    // Stage O row-major in this position's K rows: its own scores are done,
+    // and other waves only read these rows for masked keys or against zero
+    // Q padding, where the values do not matter.
     if (frame < F) {
-      bf16* orow = O + base + (size_t)frame * frame_stride + (size_t)s * D;
+      bf16* orow = ks + (size_t)(pos * F + frame) * G::KS;
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int d0 = nb * 32 + g * 8 + h * 4;
-          if (d0 < D) {
+          if (nb * 32 + g * 8 < D) {  // d0 = nb*32 + g*8 + h*4 < D (D % 8 == 0)
+            const int d0 = nb * 32 + g * 8 + h * 4;
             const uint2 w = make_uint2(pack_bf16x2(oacc[nb][g * 4 + 0] * inv, oacc[nb][g * 4 + 1] * inv),
                                        pack_bf16x2(oacc[nb][g * 4 + 2] * inv, oacc[nb][g * 4 + 3] * inv));
             *reinterpret_cast<uint2*>(orow + d0) = w;
           }
         }
+    }
+  }
+  }  // live
+  __syncthreads();
+  // O of positions s0..s0+3, all frames: each frame's run of 4*D elements is
+  // contiguous in HBM, written with 16-byte stores (same pattern as the loads).
+  for (int idx = tid; idx < total; idx += kThreads) {
+    const int frame = idx / per_frame, rem = idx % per_frame;
+    const int p = rem / G::CPR, ch = rem % G::CPR;
+    if (s0 + p < S) {
+      const size_t g = base + (size_t)frame * frame_stride + (size_t)(s0 + p) * D + ch * 8;
+      *reinterpret_cast<uint4*>(O + g) =
+          *reinterpret_cast<const uint4*>(ks + (size_t)(p * F + frame) * G::KS + ch * 8);
     }
   }
 }
