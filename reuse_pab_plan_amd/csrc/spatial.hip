@@ -7,16 +7,23 @@
 // Work split: a 256-thread block owns up to 256 query rows of one sequence,
 // 64 per wave (two 32-row MFMA blocks, so every K and V operand read from LDS
 // feeds two MFMAs; one block per wave for heads wider than 88).  Keys arrive
-// in 64-row tiles through a 3-stage LDS ring filled by direct global->LDS
-// loads (global_load_lds_dwordx4) issued two tiles ahead, so the next tiles
-// stream in while the current one computes and no registers are spent on
-// staging.  Each tile is consumed as two 32-key blocks:
+// in 64-row tiles through an LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4): each tile is a whole number of 1 KiB wave-wide
+// loads, dealt round-robin to the waves, issued two tiles ahead (four-stage
+// ring; three stages and one tile ahead where four would not leave room for
+// two blocks per CU).  No registers are spent on staging.
+//
+// Each wave walks its keys in 32-key units and software-pipelines them so the
+// matrix cores and the vector ALUs work at the same time: while the softmax of
+// unit u (exponentials, bf16 packing) runs on the VALU, the MFMAs compute the
+// scores of unit u+1 and then O^T += V^T P^T for unit u; the row maxima of
+// unit u+1 are taken under the last of those MFMAs.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of
 //     ONE query row, so row statistics need one exchange with the other
 //     half-wave;
 //   * online softmax with a lazy running max: the max is only raised when a
-//     block's max exceeds it by more than 8 (log2 units); p <= 2^8 and
-//     rescales become rare after the first blocks;
+//     unit's max exceeds it by more than 8 (log2 units); p <= 2^8 and
+//     rescales become rare after the first units;
 //   * O^T += V^T P^T: the V^T operand comes straight from the row-major V
 //     tile through ds_read_b64_tr_b16 (transposing LDS read).  Operand row D
 //     (a padding row of the last 32-row block) is set to ones, so O^T row D
@@ -24,6 +31,8 @@
 //     bf16-rounded p that multiply V -- on the MFMA.
 // Blocks are remapped so that the query tiles of one sequence share an XCD
 // (and its L2), where the sequence's K and V stay resident.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -34,7 +43,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBN = 64;                  // keys per LDS tile
-constexpr int kStages = 3;               // LDS ring depth (loads run two tiles ahead)
+constexpr int kLds = 160 * 1024;         // LDS bytes per CU
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;           // lazy-rescale threshold (log2 units)
 
@@ -74,26 +83,28 @@ struct Geo {
   // conflict-free.
   static constexpr int VS = tr_stride(D);
   static constexpr int VCH = VS / 8;
-  // Direct loads per thread per tile, rounded up; surplus slots land in the
-  // stage's tail (which also absorbs the operand over-reads past row 63).
-  static constexpr int KDMA = (kBN * KCH + kThreads - 1) / kThreads;
-  static constexpr int VDMA = (kBN * VCH + kThreads - 1) / kThreads;
-  static constexpr int KSTAGE = KDMA * kThreads * 8;  // elements
-  static constexpr int VSTAGE = VDMA * kThreads * 8;
+  // A stage is the K rows, then the V rows, then slack.  A tile is NJ
+  // wave-wide direct loads of 1 KiB (64 rows x KCH chunks = KCH loads for K,
+  // VCH for V); load j fills stage bytes [1024 j, +1024).
+  static constexpr int KREG = kBN * KS;             // elements
+  static constexpr int VREG = kBN * VS;
+  static constexpr int NJ = KCH + VCH;
+  static constexpr int NJW = (NJ + kWaves - 1) / kWaves;  // loads per wave per tile, at most
+  // Transposing reads of V past the last data column (operand rows > D, whose
+  // products are discarded) may run past the V rows into this slack.
+  static constexpr int VSLACK = 64;
+  static constexpr int STAGE = KREG + VREG + VSLACK;
+  static constexpr int NST = (2 * 4 * STAGE * 2 <= kLds) ? 4 : 3;  // ring depth
   // The last 32-row O^T block holds row D (the denominator); with no data in
   // it (D % 32 == 0) its V^T operand is a constant and is not read.
   static constexpr bool LAST_READ = (NB - 1) * 32 < D;
-  // Transposing reads of V past the last data column (operand rows > D, whose
-  // products are discarded) may run past the stage's slots into this slack.
-  static constexpr int VSLACK = 64;
-  static constexpr int STAGE = KSTAGE + VSTAGE + VSLACK;
   // K over-reads (d >= D, multiplied by Q's zero padding) must hit finite
-  // data: they stay inside the DMA'd slots, surplus slots included.
-  static_assert(kBN * KS + 8 <= KSTAGE, "K over-read must stay in the DMA'd slots");
-  static_assert((kBN - 1) * VS + (LAST_READ ? NB : NB - 1) * 32 <= VSTAGE + VSLACK,
+  // data: past the last K row they land in the V rows of the same stage.
+  static_assert((kBN - 1) * KS + ND * 16 <= KREG + VREG, "K over-read must stay in loaded rows");
+  static_assert((kBN - 1) * VS + (LAST_READ ? NB : NB - 1) * 32 <= VREG + VSLACK,
                 "V over-read must stay in the stage");
-  static_assert(kStages * STAGE * 2 <= 160 * 1024, "LDS ring too large");
-  static_assert(KDMA + VDMA < 32, "vmcnt budget");
+  static_assert(NST * STAGE * 2 <= kLds, "LDS ring too large");
+  static_assert((NST - 2) * NJW < 64, "vmcnt budget");
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
@@ -133,7 +144,8 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
                                                              bf16* __restrict__ O, int S, int nqt,
                                                              int nblocks, float c) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) bf16 ring[kStages * G::STAGE];
+  constexpr int QB = G::QB;
+  __shared__ __attribute__((aligned(16))) bf16 ring[G::NST * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -148,11 +160,11 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   bf16* __restrict__ Os = O + base;
 
   // This wave's query rows as the B operand (Q^T), resident in registers.
-  const int qrow0 = qt * G::BM + wave * 32 * G::QB;
+  const int qrow0 = qt * G::BM + wave * 32 * QB;
   const bool wave_live = qrow0 < S;
-  bf16x8 qreg[G::QB][G::ND];
+  bf16x8 qreg[QB][G::ND];
 #pragma unroll
-  for (int qb = 0; qb < G::QB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int qrow = qrow0 + qb * 32 + l32;
 #pragma unroll
     for (int ds = 0; ds < G::ND; ++ds) {
@@ -167,190 +179,266 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   // at the first use of Q inside the loop.
   wait_vmcnt<0>();
 
-  // Direct-load plan of this thread: slot s = i*256 + tid of the K (V) stage
-  // holds chunk (row, ch) = (s / KCH, s % KCH) of the tile.  Pad chunks
-  // (ch >= D/8) and surplus slots re-read chunk 0 of the tile: finite values
-  // that nothing uses.  Byte offsets are relative to the tile's first row.
-  uint32_t koff[G::KDMA], voff[G::VDMA];
+  // Direct-load plan of this wave: loads j = wave + 4i.  Load j covers stage
+  // slots 64 j .. 64 j + 63; slot s of the K (V) rows is chunk
+  // (row, ch) = (s / KCH, s % KCH) (V: VCH).  Pad chunks (ch >= D/8) re-read
+  // chunk 0 of the tile: finite values that nothing uses.  Byte offsets are
+  // relative to the tile's first row.
+  uint32_t joff[G::NJW];
 #pragma unroll
-  for (int i = 0; i < G::KDMA; ++i) {
-    const int s = i * kThreads + tid, row = s / G::KCH, ch = s % G::KCH;
-    koff[i] = (row < kBN && ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
+  for (int i = 0; i < G::NJW; ++i) {
+    const int j = wave + kWaves * i;
+    const bool is_k = j < G::KCH;
+    const int cs = is_k ? G::KCH : G::VCH;
+    const int s = (is_k ? j : j - G::KCH) * kWave + lane;
+    const int row = s / cs, ch = s % cs;
+    joff[i] = (j < G::NJ && ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
   }
-#pragma unroll
-  for (int i = 0; i < G::VDMA; ++i) {
-    const int s = i * kThreads + tid, row = s / G::VCH, ch = s % G::VCH;
-    voff[i] = (row < kBN && ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
-  }
+  const int nj_wave = (G::NJ - wave + kWaves - 1) / kWaves;  // loads this wave issues per tile
   const uint32_t ring_lds = (uint32_t)(uintptr_t)LDS_PTR(void, ring);
-  const uint32_t wave_slot = (uint32_t)(wave * kWave * 16);
+  const int nt = (S + kBN - 1) / kBN;
+  auto stage_base = [&](int t) -> uint32_t {
+    return ring_lds + (uint32_t)((t % G::NST) * G::STAGE * 2);
+  };
   auto issue = [&](int t) {
     const int key0 = t * kBN;
-    const uint32_t st = ring_lds + (uint32_t)((t % kStages) * G::STAGE * 2) + wave_slot;
+    const uint32_t st = stage_base(t);
     if (key0 + kBN <= S) {
       const bf16* kt = Ks + (size_t)key0 * D;
       const bf16* vt = Vs + (size_t)key0 * D;
 #pragma unroll
-      for (int i = 0; i < G::KDMA; ++i) dma16(kt, koff[i], st + (uint32_t)(i * kThreads * 16));
-#pragma unroll
-      for (int i = 0; i < G::VDMA; ++i)
-        dma16(vt, voff[i], st + (uint32_t)(G::KSTAGE * 2 + i * kThreads * 16));
+      for (int i = 0; i < G::NJW; ++i) {
+        const int j = wave + kWaves * i;
+        if (i + 1 < G::NJW || j < G::NJ) dma16(j < G::KCH ? kt : vt, joff[i], st + (uint32_t)(j * 1024));
+      }
     } else {
       // Ragged last tile: rows past S repeat row S-1 (finite; their scores
       // are masked and their p are 0).
 #pragma unroll
-      for (int i = 0; i < G::KDMA; ++i) {
-        const int s = i * kThreads + tid, row = s / G::KCH, ch = s % G::KCH;
-        const int r = min(key0 + min(row, kBN - 1), S - 1);
-        const uint32_t off = (row < kBN && ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
-        dma16(Ks, off, st + (uint32_t)(i * kThreads * 16));
-      }
-#pragma unroll
-      for (int i = 0; i < G::VDMA; ++i) {
-        const int s = i * kThreads + tid, row = s / G::VCH, ch = s % G::VCH;
-        const int r = min(key0 + min(row, kBN - 1), S - 1);
-        const uint32_t off = (row < kBN && ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
-        dma16(Vs, off, st + (uint32_t)(G::KSTAGE * 2 + i * kThreads * 16));
+      for (int i = 0; i < G::NJW; ++i) {
+        const int j = wave + kWaves * i;
+        if (i + 1 < G::NJW || j < G::NJ) {
+          const bool is_k = j < G::KCH;
+          const int cs = is_k ? G::KCH : G::VCH;
+          const int s = (is_k ? j : j - G::KCH) * kWave + lane;
+          const int row = s / cs, ch = s % cs;
+          const int r = min(key0 + row, S - 1);
+          const uint32_t off = (ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
+          dma16(is_k ? Ks : Vs, off, st + (uint32_t)(j * 1024));
+        }
       }
     }
   };
+  // Barrier B_t: tile t has landed and is visible to every wave; the stage
+  // read last by unit 2t-3 is free again and is refilled with the tile
+  // NST-2 ahead.
+  auto sync_tile = [&](int t) {
+    if (G::NST == 4 && t + 1 < nt) {  // tile t+1 may still be in flight
+      if (nj_wave == G::NJW) {
+        wait_vmcnt<G::NJW>();
+      } else {
+        wait_vmcnt<(G::NJW > 1 ? G::NJW - 1 : 0)>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (t + G::NST - 2 < nt) issue(t + G::NST - 2);
+  };
 
-  // Per-lane LDS bases of the operand reads; the rest of each address is a
+  issue(0);
+  if (G::NST == 4 && nt > 1) issue(1);
+
+  if (!wave_live) {
+    // Idle waves still fetch their share of every tile.
+    for (int t = 0; t < nt; ++t) sync_tile(t);
+    return;
+  }
+
+  // Per-lane LDS offsets of the operand reads; the rest of each address is a
   // compile-time offset.  Transposing V read: lane j of a 16-lane group
   // addresses row j/4 and columns 4*(j%4)..+3 of a 4x16 block and receives
   // column j, i.e. V^T row d = l32 of the operand.
   const int g16 = lane >> 4, j16 = lane & 15;
   const uint32_t klane = (uint32_t)((l32 * G::KS + h * 8) * 2);
-  const uint32_t vlane =
-      (uint32_t)(((h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 + (j16 & 3) * 4) * 2);
+  const uint32_t vlane = (uint32_t)((G::KREG + (h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 +
+                                     (j16 & 3) * 4) * 2);
   // Operand row D of V^T (the ones row) lives in lane D % 32 of block D / 32.
   const bool ones_lane = l32 == (D % 32);
   const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
 
-  f32x16 oacc[G::QB][G::NB];
+  f32x16 oacc[QB][G::NB];
 #pragma unroll
-  for (int qb = 0; qb < G::QB; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) oacc[qb][nb] = zero16();
-  float mrow[G::QB];
+  float mrow[QB];
 #pragma unroll
-  for (int qb = 0; qb < G::QB; ++qb) mrow[qb] = -INFINITY;  // log2 domain (score * c)
+  for (int qb = 0; qb < QB; ++qb) mrow[qb] = -INFINITY;  // log2 domain (score * c)
 
-  const int nt = (S + kBN - 1) / kBN;
-  issue(0);
-  if (nt > 1) issue(1);
-
-  for (int t = 0; t < nt; ++t) {
-    // Tile t has landed once at most one tile's loads are still in flight.
-    if (t + 1 < nt) {
-      wait_vmcnt<G::KDMA + G::VDMA>();
-    } else {
-      wait_vmcnt<0>();
+  // S^T block of the 32 keys at row kb*32 of the stage whose K rows `kaddr`
+  // points into (per-lane offset included).
+  auto qk = [&](uint32_t kaddr, int kb, f32x16 (&s)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = zero16();
+#pragma unroll
+    for (int ds = 0; ds < G::ND; ++ds) {
+      const bf16x8 a = *LDS_PTR(const bf16x8, kaddr + (uint32_t)((kb * 32 * G::KS + ds * 16) * 2));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32(a, qreg[qb][ds], s[qb]);
     }
-    __syncthreads();
-    if (t + 2 < nt) issue(t + 2);  // refills the stage read in iteration t-1
-    if (wave_live) {
-      const uint32_t stage = ring_lds + (uint32_t)((t % kStages) * G::STAGE * 2);
-      const uint32_t kaddr = opaque(stage + klane);
-      const uint32_t vaddr = opaque(stage + (uint32_t)(G::KSTAGE * 2) + vlane);
-      const int key0 = t * kBN;
+  };
+  // Keys >= S do not exist.
+  auto mask = [&](f32x16 (&s)[QB], int key_first) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc[G::QB];
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int qb = 0; qb < G::QB; ++qb) sacc[qb] = zero16();
+      for (int r = 0; r < 16; ++r)
+        if (key_first + acc_row(r, h) >= S) s[qb][r] = -INFINITY;
+  };
+  auto rowmax = [&](const f32x16 (&s)[QB], float (&mx)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ds = 0; ds < G::ND; ++ds) {
-          const bf16x8 a =
-              *LDS_PTR(const bf16x8, kaddr + (uint32_t)((kb * 32 * G::KS + ds * 16) * 2));
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = s[qb][0];
 #pragma unroll
-          for (int qb = 0; qb < G::QB; ++qb) sacc[qb] = mfma32(a, qreg[qb][ds], sacc[qb]);
-        }
-        if (key0 + kb * 32 + 32 > S) {  // ragged end: keys >= S do not exist
-#pragma unroll
-          for (int qb = 0; qb < G::QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (key0 + kb * 32 + acc_row(r, h) >= S) sacc[qb][r] = -INFINITY;
-        }
-        bf16x8 pb[G::QB][2];
-#pragma unroll
-        for (int qb = 0; qb < G::QB; ++qb) {
-          float mx = sacc[qb][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-          mx = max_halves(mx);
-          const float mnew = mx * c;
-          if (mnew > mrow[qb] + kSlack) {
-            const float alpha = fast_exp2(mrow[qb] - mnew);
-#pragma unroll
-            for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
-            mrow[qb] = mnew;
-          }
-          const float negm = -mrow[qb];
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            const int r0 = t2 * 8;
-            pb[qb][t2] = to_bf16x8(
-                fast_exp2(fmaf(sacc[qb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[qb][r0 + 1], c, negm)),
-                fast_exp2(fmaf(sacc[qb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[qb][r0 + 3], c, negm)),
-                fast_exp2(fmaf(sacc[qb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[qb][r0 + 5], c, negm)),
-                fast_exp2(fmaf(sacc[qb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[qb][r0 + 7], c, negm)));
-          }
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-          for (int nb = 0; nb < G::NB; ++nb) {
-            bf16x8 a;
-            if (nb < G::NB - 1 || G::LAST_READ) {
-              const uint32_t p = vaddr + (uint32_t)(((kb * 32 + t2 * 16) * G::VS + nb * 32) * 2);
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
-              const i16x4 hi =
-                  __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
-              a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-              if (nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
-                uint4 w = __builtin_bit_cast(uint4, a);
-                w.x = ones_lane ? ones_word : w.x;
-                w.y = ones_lane ? ones_word : w.y;
-                w.z = ones_lane ? ones_word : w.z;
-                w.w = ones_lane ? ones_word : w.w;
-                a = __builtin_bit_cast(bf16x8, w);
-              }
-            } else {
-              a = __builtin_bit_cast(bf16x8, make_uint4(ones_word, ones_word, ones_word, ones_word));
-            }
-#pragma unroll
-            for (int qb = 0; qb < G::QB; ++qb) oacc[qb][nb] = mfma32(a, pb[qb][t2], oacc[qb][nb]);
-          }
-        }
-      }
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][r]);
+      mx[qb] = max_halves(m);
     }
-  }
-
-  if (wave_live) {
+  };
+  // Raise the running max where a unit's max exceeds it by more than the
+  // slack, rescaling what has been accumulated so far.
+  auto rescale = [&](const float (&mx)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < G::QB; ++qb) {
-      const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
-      const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
-      const int qrow = qrow0 + qb * 32 + l32;
-      if (qrow < S) {
-        bf16* orow = Os + (size_t)qrow * D;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mnew = mx[qb] * c;
+      if (mnew > mrow[qb] + kSlack) {
+        const float alpha = fast_exp2(mrow[qb] - mnew);
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d0 = nb * 32 + g * 8 + h * 4;
-            if (d0 < D) {
-              const uint2 w =
-                  make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
-                             pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
-              *reinterpret_cast<uint2*>(orow + d0) = w;
-            }
-          }
+          for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
+        mrow[qb] = mnew;
       }
+    }
+  };
+  // P^T operand (bf16) of scores r0..r0+7 (r0 = 8*t2): 16 keys per lane half.
+  auto probs = [&](const f32x16 (&s)[QB], int t2, bf16x8 (&pb)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float negm = -mrow[qb];
+      const int r0 = t2 * 8;
+      pb[qb] = to_bf16x8(
+          fast_exp2(fmaf(s[qb][r0 + 0], c, negm)), fast_exp2(fmaf(s[qb][r0 + 1], c, negm)),
+          fast_exp2(fmaf(s[qb][r0 + 2], c, negm)), fast_exp2(fmaf(s[qb][r0 + 3], c, negm)),
+          fast_exp2(fmaf(s[qb][r0 + 4], c, negm)), fast_exp2(fmaf(s[qb][r0 + 5], c, negm)),
+          fast_exp2(fmaf(s[qb][r0 + 6], c, negm)), fast_exp2(fmaf(s[qb][r0 + 7], c, negm)));
+    }
+  };
+  // O^T += V^T P^T over keys kb*32 + 16*t2 .. +15 of the stage whose V rows
+  // `vaddr` points into (per-lane offset included).
+  auto pv = [&](uint32_t vaddr, int kb, int t2, const bf16x8 (&pb)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) {
+      bf16x8 a;
+      if (nb < G::NB - 1 || G::LAST_READ) {
+        const uint32_t p = vaddr + (uint32_t)(((kb * 32 + t2 * 16) * G::VS + nb * 32) * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
+        a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if (nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
+          uint4 w = __builtin_bit_cast(uint4, a);
+          w.x = ones_lane ? ones_word : w.x;
+          w.y = ones_lane ? ones_word : w.y;
+          w.z = ones_lane ? ones_word : w.z;
+          w.w = ones_lane ? ones_word : w.w;
+          a = __builtin_bit_cast(bf16x8, w);
+        }
+      } else {
+        a = __builtin_bit_cast(bf16x8, make_uint4(ones_word, ones_word, ones_word, ones_word));
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma32(a, pb[qb], oacc[qb][nb]);
+    }
+  };
+  // One pipelined unit: softmax and PV of the current unit (scores `sc`, V at
+  // row kb_cur*32 of `v_cur`) around the QK of the next unit (K at row
+  // kb_next*32 of `k_next`, scores into `sn`, row maxima into `mxn`).  The
+  // MFMA and VALU streams sit in one basic block, so the scheduler can
+  // interleave them.  With `masked`, keys of the next unit from S on are
+  // masked (only the last tile has such keys).
+  auto unit = [&](auto masked, uint32_t k_next, int kb_next, int key_next, uint32_t v_cur,
+                  int kb_cur, const f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&mxn)[QB])
+      __attribute__((always_inline)) {
+    bf16x8 p0[QB], p1[QB];
+    qk(k_next, kb_next, sn);
+    probs(sc, 0, p0);
+    pv(v_cur, kb_cur, 0, p0);
+    probs(sc, 1, p1);
+    pv(v_cur, kb_cur, 1, p1);
+    if constexpr (decltype(masked)::value) mask(sn, key_next);
+    rowmax(sn, mxn);
+  };
+
+  f32x16 sA[QB], sB[QB];
+  float mA[QB], mB[QB];
+
+  sync_tile(0);
+  {
+    const uint32_t st = stage_base(0);
+    qk(opaque(st + klane), 0, sA);
+    if (S < 32) mask(sA, 0);
+    rowmax(sA, mA);
+  }
+
+  // One tile per iteration: units 2t (scores in sA) and 2t+1, each with the
+  // QK of the unit after it underneath.  While both of those units have all
+  // 32 keys below S the iteration needs no masking.
+  const int UF = S / 32;   // units with all 32 keys present
+  int t = 0;
+  for (; 2 * t + 2 < UF; ++t) {
+    const uint32_t cur = stage_base(t);
+    const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
+    rescale(mA);
+    unit(std::false_type{}, kc, 1, 0, vc, 0, sA, sB, mB);
+    rescale(mB);
+    sync_tile(t + 1);
+    const uint32_t kn = opaque(stage_base(t + 1) + klane);
+    unit(std::false_type{}, kn, 0, 0, vc, 1, sB, sA, mA);
+  }
+  // The last one or two tiles, masked.  A unit entirely past S (the second
+  // unit of the last tile when S % 64 is 1..32) has all p exactly 0 and
+  // changes nothing; the QK after the last unit runs on stale but in-bounds
+  // LDS and is dropped.
+  for (; t < nt; ++t) {
+    const uint32_t cur = stage_base(t);
+    const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
+    rescale(mA);
+    unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB, mB);
+    rescale(mB);
+    if (t + 1 < nt) sync_tile(t + 1);
+    const uint32_t kn = opaque(stage_base(t + 1) + klane);
+    unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA, mA);
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
+    const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+    const int qrow = qrow0 + qb * 32 + l32;
+    if (qrow < S) {
+      bf16* orow = Os + (size_t)qrow * D;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = nb * 32 + g * 8 + h * 4;
+          if (d0 < D) {
+            const uint2 w =
+                make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
+                           pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
+            *reinterpret_cast<uint2*>(orow + d0) = w;
+          }
+        }
     }
   }
 }

@@ -3,14 +3,16 @@
 //
 // Per (b, h, s): O[:, s] = softmax(Q[:, s] K[:, s]^T * scale) V[:, s] over the
 // F <= 64 frames.  Short sequences, HBM-bound (about 24 flop per byte at
-// F = 48, D = 72), so the design is about moving bytes: a 256-thread block
-// takes 4 consecutive token positions of one (b, h); for every frame those
-// positions are one contiguous run of 4*D elements, read as 16-byte vectors
+// F = 48, D = 72), so the design is about moving bytes: a 128-thread block
+// takes 2 consecutive token positions of one (b, h) (small blocks, so several
+// share a CU and their load, compute and store phases overlap); for every frame
+// those positions are one contiguous run of 2*D elements, read as 16-byte vectors
 // into LDS (K and V row-major, a frame column per position).  Each wave then
 // owns one position: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q loaded
 // straight into registers, a full-row softmax (no running max needed), and
-// O^T = V^T P^T with the V^T operand gathered from the row-major LDS copy and
-// an implicit all-ones row D that yields the softmax denominator.
+// O^T = V^T P^T with the V^T operand taken by transposing LDS reads
+// (ds_read_b64_tr_b16) of the row-major copy and an all-ones operand row D that
+// yields the softmax denominator.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -18,9 +20,11 @@ namespace pab {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 2;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kPos = kWaves;        // token positions per block (one per wave)
+constexpr int kSlack = 64;          // elements after V: transposing over-read of the last row
+
 constexpr int kPadRows = 32;        // zero rows after the last position (frame over-read)
 constexpr int kBatch = 8;           // 16-byte loads in flight per thread while filling LDS
 constexpr float kLog2e = 1.4426950408889634f;
@@ -36,7 +40,9 @@ struct Geo {
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
 };
 
-__device__ __forceinline__ uint16_t bits16(bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restrict__ Q,
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
     ks[(size_t)kPos * F * G::KS + i] = (bf16)0.f;
     vs[(size_t)kPos * F * G::KS + i] = (bf16)0.f;
   }
-  // K, V of positions s0..s0+3, all frames -> LDS row (pos*F + frame).
+  // K, V of positions s0..s0+kPos-1, all frames -> LDS row (pos*F + frame).
   const int per_frame = kPos * G::CPR;      // 16-byte chunks per frame run
   const int total = F * per_frame;
   for (int b0 = 0; b0 < total; b0 += kThreads * kBatch) {
@@ -119,23 +125,33 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   const bf16* vp = vs + (size_t)pos * F * G::KS;
   const int nsteps = (F + 15) / 16;   // 16-frame PV steps
 
-  // V^T operand for output block nb, PV step t: V[frames 16t + {h*4+j, 8+h*4+j}][d].
+  // V^T operand for output block nb, PV step t (frames 16t + {h*4+j, 8+h*4+j})
+  // by transposing LDS reads of the row-major V: lane j of a 16-lane group
+  // addresses frame row j/4, columns 4*(j%4)..+3 of a 4x16 block and receives
+  // column j (operand row d = l32).  Operand row D is ones (the softmax
+  // denominator); rows > D are don't-care.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const bf16* vlane = vp + (h * 4 + (j16 >> 2)) * G::KS + (g16 & 1) * 16 + (j16 & 3) * 4;
+  const bool ones_lane = l32 == (D % 32);
+  const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
   auto v_operand = [&](int nb, int t) -> bf16x8 {
-    const int d = nb * 32 + l32;
-    bf16x8 a;
-    if (d < D) {
-      const bf16* col = vp + d;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int frame = t * 16 + (j >> 2) * 8 + h * 4 + (j & 3);
-        a[j] = col[(size_t)frame * G::KS];
+    uint4 w;
+    if (nb * 32 < D) {
+      const bf16* p = vlane + t * 16 * G::KS + nb * 32;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::KS));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      w = make_uint4(l2.x, l2.y, h2.x, h2.y);
+      if ((nb + 1) * 32 > D) {
+        w.x = ones_lane ? ones_word : w.x;
+        w.y = ones_lane ? ones_word : w.y;
+        w.z = ones_lane ? ones_word : w.z;
+        w.w = ones_lane ? ones_word : w.w;
       }
     } else {
-      const bf16 val = (bf16)(d == D ? 1.f : 0.f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = val;
+      w = make_uint4(ones_word, ones_word, ones_word, ones_word);
     }
-    return a;
+    return __builtin_bit_cast(bf16x8, w);
   };
 
   // Phase 1: probabilities of both 32-frame query blocks.  All reads of K
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   }
   }  // live
   __syncthreads();
-  // O of positions s0..s0+3, all frames: each frame's run of 4*D elements is
+  // O of positions s0..s0+kPos-1, all frames: each frame's run of kPos*D elements is
   // contiguous in HBM, written with 16-byte stores (same pattern as the loads).
   for (int idx = tid; idx < total; idx += kThreads) {
     const int frame = idx / per_frame, rem = idx % per_frame;
@@ -238,7 +254,7 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, int64_
   const int pos_blocks = (S + kPos - 1) / kPos;
   const int64_t nblocks = nbh * pos_blocks;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const size_t lds = 2 * (size_t)(kPos * F + kPadRows) * Geo<D>::KS * sizeof(bf16);
+  const size_t lds = (2 * (size_t)(kPos * F + kPadRows) * Geo<D>::KS + kSlack) * sizeof(bf16);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&temporal_kernel<D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
