@@ -14,12 +14,14 @@
 //     the padding column d = D carries a key bias (0 for real keys, -1e30 for
 //     the padding keys past L) against a 1 in Q, so padding keys are masked
 //     by the MFMA itself.
-//   * The V^T operand comes from the row-major V through ds_read_b64_tr_b16,
-//     with its padding row D set to ones so the MFMA emits the softmax
-//     denominator.
-//   * Q of the tile two ahead is loaded while the current one computes
-//     (non-temporal: each byte is read once); each wave's output tile is
-//     staged in LDS and written with lane-contiguous 16-byte stores.
+//   * The V^T operand comes from the row-major V through ds_read_b64_tr_b16;
+//     V carries a column D of ones (zeros past L), so O^T row D is the
+//     softmax denominator, summed on the MFMA.
+//   * A 32-row query tile is one contiguous run in HBM: it is copied into a
+//     per-wave two-stage LDS ring by direct global->LDS loads (whole-line
+//     requests, no staging registers), the next tile's loads running while
+//     the current one computes; the tile's output is staged row-major in the
+//     same stage and written with lane-contiguous 16-byte stores.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -58,17 +60,46 @@ constexpr int odd_chunk_stride(int min_elems) {
   return ((s / 8) % 2) ? s : s + 8;
 }
 
+// One 16-byte direct global->LDS load per lane: lane l of the wave reads
+// global bytes [gbase + voff, +16) and writes LDS bytes [lds + 16*l, +16).
+// `gbase` and `lds` must be wave-uniform.  Issued from inline assembly so that
+// its wait (s_waitcnt vmcnt) is placed by hand; the instruction has no
+// result register.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 template <int D, int NKB>
 struct Geo {
   static constexpr int ND = (D + 15) / 16;             // 16-wide d steps of Q K^T
   static constexpr int NB = D / 32 + 1;                // 32-row blocks of O^T
   static constexpr bool BIAS = (D % 16) != 0;          // padding column d = D exists
-  static constexpr int KS = odd_chunk_stride(BIAS ? D + 8 : D);
+  static constexpr int KS = BIAS ? D + 8 : odd_chunk_stride(D);
   static constexpr int KROWS = NKB * 32 + 1;           // +1: keeps row reads in bounds
-  static constexpr int VS = tr_stride(D);
+  // The last 32-row O^T block holds data rows and the denominator row D: V
+  // then carries a column D of ones (zeros past L) so the operand needs no
+  // per-use fix-up.
+  static constexpr bool ONES_COL = (D % 32) != 0;
+  static constexpr int VS = tr_stride(ONES_COL ? D + 1 : D);
   static constexpr int VROWS = NKB * 32;
   static constexpr int VSLACK = 64;                    // transposing over-read past the last row
   static constexpr int CPR = D / 8;                    // 16-byte chunks per input row
+  // A 32-row query tile is contiguous in HBM: NQJ wave-wide 1 KiB direct
+  // loads fill one stage of the wave's two-stage ring, which later also
+  // stages the tile's output.
+  static constexpr int NQJ = (32 * D * 2 + 1023) / 1024;
+  static constexpr int QSTAGE = 32 * D;                // elements; the last load is partial
+  static constexpr int NOST = (32 * D / 8 + kWave - 1) / kWave;  // output stores per tile
   static constexpr bool LAST_READ = (NB - 1) * 32 < D;
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
@@ -85,8 +116,9 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
   using G = Geo<D, NKB>;
   __shared__ __attribute__((aligned(16))) bf16 ks[G::KROWS * G::KS];
   __shared__ __attribute__((aligned(16))) bf16 vs[G::VROWS * G::VS + G::VSLACK];
-  // Per-wave output tile (32 rows x D, row-major).
-  __shared__ __attribute__((aligned(16))) bf16 ostage[kWaves][32 * D];
+  // Per-wave two-stage ring of query tiles (each stage later holds the
+  // tile's output, row-major).
+  __shared__ __attribute__((aligned(16))) bf16 qstage[kWaves][2][G::QSTAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -127,6 +159,14 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
         if (row < G::VROWS) *reinterpret_cast<uint4*>(&vs[row * G::VS + ch * 8]) = vr[it];
       }
     }
+    // Columns D..VS-1 of every V row: ones at d = D for real keys, zeros
+    // elsewhere.
+    if (G::ONES_COL) {
+      for (int i = tid; i < G::VROWS; i += kThreads) {
+#pragma unroll
+        for (int d = D; d < G::VS; ++d) vs[i * G::VS + d] = (bf16)((d == D && i < L) ? 1.f : 0.f);
+      }
+    }
     // Columns D..KS-1 of every K row: the key bias at d = D (when it exists),
     // zeros after it.
     for (int i = tid; i < G::KROWS; i += kThreads) {
@@ -148,35 +188,44 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
       vs_lds + (uint32_t)(((h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 + (j16 & 3) * 4) * 2);
   const uint32_t ks_lds = (uint32_t)(uintptr_t)LDS_PTR(void, ks);
   const uint32_t klane = ks_lds + (uint32_t)((l32 * G::KS + h * 8) * 2);
-  const bool ones_lane = l32 == (D % 32);
-  const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
+  // With D % 32 == 0 the last O^T block is the ones row alone (lane 0).
+  const uint32_t ones_word = l32 == 0 ? 0x3F803F80u : 0u;
   // Q padding word at d = D (1 in its low half) when the bias column is used.
   const uint32_t qpad_word = G::BIAS ? 0x00003F80u : 0u;
 
-  // Q tile (B operand, Q^T) as 32-bit words: lane (row l32, half h) holds
-  // d = ds*16 + h*8 .. +7 for each d step.
-  auto load_q = [&](u32x4 (&qr)[G::ND], int tile) {
-    const int64_t row = (int64_t)tile * 32 + l32;
-    const bool live = row < nq;
+  // Direct loads of query tile `tile` into stage `st` (LDS byte address):
+  // lane l of load j copies tile bytes [1024 j + 16 l, +16), clamped to the
+  // tile's last valid 16 bytes (rows past nq re-read it: finite values whose
+  // outputs are not stored).
+  auto issue_q = [&](int tile, uint32_t st) {
+    const int64_t rows_left = nq - (int64_t)tile * 32;
+    const uint32_t valid = (uint32_t)((rows_left >= 32 ? 32 : rows_left) * D * 2);
+    const bf16* tb = Qh + (int64_t)tile * 32 * D;
 #pragma unroll
-    for (int ds = 0; ds < G::ND; ++ds) {
-      const int d0 = ds * 16 + h * 8;
-      if (ds * 16 + 8 < D) {  // both halves hold data
-        qr[ds] = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Qh + row * D + d0))
-                      : u32x4{0u, 0u, 0u, 0u};
-      } else {  // last step of a D % 16 == 8 head: the upper half is padding
-        const u32x4 pad = {qpad_word, 0u, 0u, 0u};
-        qr[ds] = (h == 0 && live)
-                     ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Qh + row * D + d0))
-                     : (h == 0 ? u32x4{0u, 0u, 0u, 0u} : pad);
-      }
+    for (int j = 0; j < G::NQJ; ++j) {
+      const uint32_t pos = (uint32_t)(j * 1024 + lane * 16);
+      const uint32_t off = min(pos, valid - 16u);
+      // Lanes past the stage stay idle (their LDS bytes are not written).
+      if (j + 1 < G::NQJ || pos < (uint32_t)(32 * D * 2)) dma16(tb, off, st + (uint32_t)(j * 1024));
     }
   };
 
   // One 32-row query tile against the text keys: full-row softmax,
   // O = P V / sum(P) on the MFMA, row-major staging, coalesced stores.
-  bf16* ost = ostage[wave];
-  auto compute = [&](const u32x4 (&q)[G::ND], int tile) {
+  auto compute = [&](bf16* ost, int tile) {
+    // Q^T operand: lane (row l32, half h) holds d = ds*16 + h*8 .. +7.
+    const uint32_t qlane = (uint32_t)(uintptr_t)LDS_PTR(void, ost) + (uint32_t)((l32 * D + h * 8) * 2);
+    u32x4 q[G::ND];
+#pragma unroll
+    for (int ds = 0; ds < G::ND; ++ds) {
+      if (ds * 16 + 8 < D) {  // both halves hold data
+        q[ds] = *LDS_PTR(const u32x4, qlane + (uint32_t)(ds * 32));
+      } else {  // last step of a D % 16 == 8 head: the upper half is padding
+        const u32x4 pad = {qpad_word, 0u, 0u, 0u};
+        const u32x4 lo = *LDS_PTR(const u32x4, qlane + (uint32_t)(ds * 32) - (uint32_t)(h * 16));
+        q[ds] = h == 0 ? lo : pad;
+      }
+    }
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -221,13 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
             const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-            a = u32x4{l2.x, l2.y, h2.x, h2.y};
-            if (nb == G::NB - 1) {  // operand rows > D are don't-care; row D is ones
-              a.x = ones_lane ? ones_word : a.x;
-              a.y = ones_lane ? ones_word : a.y;
-              a.z = ones_lane ? ones_word : a.z;
-              a.w = ones_lane ? ones_word : a.w;
-            }
+            a = u32x4{l2.x, l2.y, h2.x, h2.y};  // operand rows > D are don't-care
           } else {
             a = u32x4{ones_word, ones_word, ones_word, ones_word};
           }
@@ -265,22 +308,25 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
     __builtin_amdgcn_wave_barrier();
   };
 
-  // This wave's tiles: t_begin + wave, + 4, + 8, ...  Q of the tile two
-  // ahead is loaded while the current one computes (three register sets).
-  u32x4 qa[G::ND], qb[G::ND], qc[G::ND];
-  int tile = t_begin + wave;
-  constexpr int step = kWaves;
-  if (tile < t_end) load_q(qa, tile);
-  if (tile + step < t_end) load_q(qb, tile + step);
-  for (; tile < t_end; tile += 3 * step) {
-    if (tile + 2 * step < t_end) load_q(qc, tile + 2 * step);
-    compute(qa, tile);
-    if (tile + step >= t_end) break;
-    if (tile + 3 * step < t_end) load_q(qa, tile + 3 * step);
-    compute(qb, tile + step);
-    if (tile + 2 * step >= t_end) break;
-    if (tile + 4 * step < t_end) load_q(qb, tile + 4 * step);
-    compute(qc, tile + 2 * step);
+  // This wave's tiles: t_begin + wave, + 4, + 8, ...; tile k of the wave
+  // sits in stage k % 2, and the next tile's loads run while one computes.
+  // vmcnt accounting: after the loads of tile k come the stores of tile k-1
+  // (NOST instructions, always a full tile) and the loads of tile k+1 (NQJ).
+  const uint32_t st0 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][0]);
+  const uint32_t st1 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][1]);
+  const int first = t_begin + wave;
+  const int n = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
+  if (n > 0) issue_q(first, st0);
+  for (int k = 0; k < n; ++k) {
+    const int tile = first + k * kWaves;
+    const bool more = k + 1 < n;
+    if (more) issue_q(tile + kWaves, (k & 1) ? st0 : st1);
+    if (k >= 1) {
+      if (more) wait_vmcnt<G::NOST + G::NQJ>(); else wait_vmcnt<G::NOST>();
+    } else {
+      if (more) wait_vmcnt<G::NQJ>(); else wait_vmcnt<0>();
+    }
+    compute(qstage[wave][k & 1], tile);
   }
 }
 

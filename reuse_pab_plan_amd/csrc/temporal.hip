@@ -64,6 +64,23 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   const int64_t frame_stride = (int64_t)S * D;
   const size_t base = (size_t)bh * F * frame_stride;
 
+  // This wave's position: Q^T operand straight from HBM, loaded first so that
+  // it is in flight together with the K and V loads below.
+  const int pos = wave;
+  const int s = s0 + pos;
+  const bool live = s < S;
+  const int nqb = (F + 31) / 32;   // query (and key) blocks of 32 frames: 1 or 2
+  bf16x8 qreg[2][G::ND];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ds = 0; ds < G::ND; ++ds) {
+      const int frame = qb * 32 + l32, d0 = ds * 16 + h * 8;
+      qreg[qb][ds] = (live && frame < F && d0 < D)
+                         ? *reinterpret_cast<const bf16x8*>(Q + base + (size_t)frame * frame_stride +
+                                                            (size_t)s * D + d0)
+                         : zero_bf16x8();
+    }
   // Zero the pad rows (read by the 32-frame blocks past F of the last position).
   for (int i = tid; i < kPadRows * G::KS; i += kThreads) {
     ks[(size_t)kPos * F * G::KS + i] = (bf16)0.f;
@@ -81,9 +98,9 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
       vr[u] = make_uint4(0u, 0u, 0u, 0u);
       if (idx < total) {
         const int frame = idx / per_frame, rem = idx % per_frame;
-        const int pos = rem / G::CPR, ch = rem % G::CPR;
-        if (s0 + pos < S) {
-          const size_t g = base + (size_t)frame * frame_stride + (size_t)(s0 + pos) * D + ch * 8;
+        const int p = rem / G::CPR, ch = rem % G::CPR;
+        if (s0 + p < S) {
+          const size_t g = base + (size_t)frame * frame_stride + (size_t)(s0 + p) * D + ch * 8;
           kr[u] = *reinterpret_cast<const uint4*>(K + g);
           vr[u] = *reinterpret_cast<const uint4*>(V + g);
         }
@@ -94,30 +111,14 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
       const int idx = b0 + u * kThreads + tid;
       if (idx < total) {
         const int frame = idx / per_frame, rem = idx % per_frame;
-        const int pos = rem / G::CPR, ch = rem % G::CPR;
-        const size_t l = (size_t)(pos * F + frame) * G::KS + ch * 8;
+        const int p = rem / G::CPR, ch = rem % G::CPR;
+        const size_t l = (size_t)(p * F + frame) * G::KS + ch * 8;
         *reinterpret_cast<uint4*>(ks + l) = kr[u];
         *reinterpret_cast<uint4*>(vs + l) = vr[u];
       }
     }
   }
 
-  // This wave's position: Q^T operand straight from HBM.
-  const int pos = wave;
-  const int s = s0 + pos;
-  const bool live = s < S;
-  const int nqb = (F + 31) / 32;   // query (and key) blocks of 32 frames: 1 or 2
-  bf16x8 qreg[2][G::ND];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int ds = 0; ds < G::ND; ++ds) {
-      const int frame = qb * 32 + l32, d0 = ds * 16 + h * 8;
-      qreg[qb][ds] = (live && frame < F && d0 < D)
-                         ? *reinterpret_cast<const bf16x8*>(Q + base + (size_t)frame * frame_stride +
-                                                            (size_t)s * D + d0)
-                         : zero_bf16x8();
-    }
   __syncthreads();
 
   if (live) {
