@@ -96,9 +96,10 @@ int pab_plan_schedule(int32_t num_steps, int32_t num_types, const int32_t* range
  * PAB article, "Implementation", second observation (spatial attention).
  * For every (b, h, f): O = softmax(Q K^T * scale) V over the S tokens of that
  * frame.  q, k, v, o: [B, H, F, S, D] device buffers of `dtype`.
- * Supported: D a multiple of 8 with 8 <= D <= 128.  o must not overlap q, k
- * or v.  Full-3D self-attention over F' frames of S' tokens is this call with
- * F = 1, S = F'*S'.
+ * Supported: D a multiple of 8 with 8 <= D <= 128; for bf16 one sequence
+ * (S*D elements) must be under 4 GiB (else PAB_ERR_UNSUPPORTED).  o must not
+ * overlap q, k or v.  Full-3D self-attention over F' frames of S' tokens is
+ * this call with F = 1, S = F'*S'.
  */
 int pab_attn_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
                      int32_t F, int32_t S, int32_t D, int32_t dtype, float softmax_scale,
@@ -111,7 +112,9 @@ int pab_attn_spatial(const void* q, const void* k, const void* v, void* o, int32
  * and "Parallel" (the attention whose sequence-parallel form needs two
  * all-to-all exchanges).  For every (b, h, s): O[b,h,:,s] =
  * softmax(Q[b,h,:,s] K[b,h,:,s]^T * scale) V[b,h,:,s].  Same buffers and
- * layout as pab_attn_spatial.  Supported: D as above and 1 <= F <= 64.
+ * layout as pab_attn_spatial.  Supported: D as above and 1 <= F <= 64; for
+ * bf16 one (b, h) slab (F*S*D elements) must be under 4 GiB (else
+ * PAB_ERR_UNSUPPORTED).
  */
 int pab_attn_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
                       int32_t F, int32_t S, int32_t D, int32_t dtype, float softmax_scale,

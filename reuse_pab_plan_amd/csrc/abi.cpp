@@ -89,6 +89,12 @@ int check_video_attn(const char* fn, const void* q, const void* k, const void* v
   if (st) return st;
   if (temporal && F > 64)
     return fail(PAB_ERR_UNSUPPORTED, fmt("%s: F=%d frames unsupported (max 64)", fn, F));
+  // The bf16 kernels address one (b, h) slab (temporal) or one sequence
+  // (spatial) with 32-bit byte offsets.
+  const int64_t slab = temporal ? (int64_t)F * S * D * 2 : (int64_t)S * D * 2;
+  if (dtype == PAB_BF16 && slab >= ((int64_t)1 << 32))
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: %s of %lld bytes exceeds 4 GiB", fn,
+                                         temporal ? "(b, h) slab" : "sequence", (long long)slab));
   const size_t bytes = (size_t)n * dtype_size(dtype);
   if (ranges_overlap(o, bytes, q, bytes) || ranges_overlap(o, bytes, k, bytes) ||
       ranges_overlap(o, bytes, v, bytes))

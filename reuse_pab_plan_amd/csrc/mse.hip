@@ -16,7 +16,7 @@ namespace pab {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 2048;
+constexpr int kMaxBlocks = 4096;
 constexpr int kUnroll = 4;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

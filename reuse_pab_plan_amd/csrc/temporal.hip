@@ -3,16 +3,20 @@
 //
 // Per (b, h, s): O[:, s] = softmax(Q[:, s] K[:, s]^T * scale) V[:, s] over the
 // F <= 64 frames.  Short sequences, HBM-bound (about 24 flop per byte at
-// F = 48, D = 72), so the design is about moving bytes: a 128-thread block
-// takes 2 consecutive token positions of one (b, h) (small blocks, so several
-// share a CU and their load, compute and store phases overlap); for every frame
-// those positions are one contiguous run of 2*D elements, read as 16-byte vectors
-// into LDS (K and V row-major, a frame column per position).  Each wave then
-// owns one position: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q loaded
-// straight into registers, a full-row softmax (no running max needed), and
-// O^T = V^T P^T with the V^T operand taken by transposing LDS reads
-// (ds_read_b64_tr_b16) of the row-major copy and an all-ones operand row D that
-// yields the softmax denominator.
+// F = 48, D = 72), so the design is about moving bytes.  A 256-thread block
+// takes 4 consecutive token positions of one (b, h) (two blocks share a CU,
+// so their load, compute and store phases overlap).  For every frame those
+// positions are one contiguous run of 4*D elements in HBM; K and V
+// are copied run by run into LDS in the same frame-major order by direct
+// global->LDS loads (whole runs per request, no staging registers), while Q
+// goes straight to registers.  Each wave then owns one position:
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16, a full-row softmax (no running
+//     max needed: at most 64 frames);
+//   * O^T = V^T P^T with the V^T operand taken by transposing LDS reads
+//     (ds_read_b64_tr_b16) and an all-ones operand row D that yields the
+//     softmax denominator;
+//   * the output is staged frame-major in the K buffer and written back run
+//     by run with lane-contiguous 16-byte stores.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -20,29 +24,47 @@ namespace pab {
 
 namespace {
 
-constexpr int kWaves = 2;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kPos = kWaves;        // token positions per block (one per wave)
-constexpr int kSlack = 64;          // elements after V: transposing over-read of the last row
-
-constexpr int kPadRows = 32;        // zero rows after the last position (frame over-read)
-constexpr int kBatch = 8;           // 16-byte loads in flight per thread while filling LDS
+constexpr int kMaxF = 64;           // frames; LDS holds 64 frame runs per tensor
+constexpr int kSlack = 64;          // elements after V: transposing over-read of the last run
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct Geo {
   static constexpr int ND = (D + 15) / 16;
   static constexpr int NB = D / 32 + 1;
-  static constexpr int KS = D;        // dense rows; odd 16-byte count not required here
-  static constexpr int CPR = D / 8;
+  static constexpr int RUN = kPos * D;           // elements per frame run (LDS row stride)
+  static constexpr int RCH = RUN / 8;            // 16-byte chunks per run
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
+  static constexpr int LDS_ELEMS = 2 * kMaxF * RUN + kSlack;
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
+// One 16-byte direct global->LDS load per lane: lane l of the wave reads
+// global bytes [gbase + voff, +16) and writes LDS bytes [lds + 16*l, +16).
+// `gbase` and `lds` must be wave-uniform.  Inline assembly, so that the wait
+// for it is placed by hand (the compiler does not track these loads).
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// A wave-uniform pointer, moved to scalar registers (the direct load takes
+// its base address from an SGPR pair).
+__device__ __forceinline__ const bf16* uniform_ptr(const bf16* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const bf16*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restrict__ Q,
@@ -51,24 +73,26 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
                                                            bf16* __restrict__ O, int F, int S,
                                                            int pos_blocks, int nblocks, float c) {
   using G = Geo<D>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int rows = kPos * F + kPadRows;   // rows per tensor in LDS
-  bf16* ks = reinterpret_cast<bf16*>(smem);
-  bf16* vs = ks + (size_t)rows * G::KS;
+  __shared__ __attribute__((aligned(16))) bf16 smem[G::LDS_ELEMS];
+  bf16* ks = smem;                     // K runs, frame-major: row f holds positions 0..kPos-1
+  bf16* vs = smem + kMaxF * G::RUN;    // V runs
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int logical = xcd_remap(blockIdx.x, nblocks);
   const int64_t bh = logical / pos_blocks;
   const int s0 = (logical % pos_blocks) * kPos;
   const int64_t frame_stride = (int64_t)S * D;
   const size_t base = (size_t)bh * F * frame_stride;
+  // Positions of this block that exist (the last block of a (b, h) may hold one).
+  const int npos = min(kPos, S - s0);
 
-  // This wave's position: Q^T operand straight from HBM, loaded first so that
-  // it is in flight together with the K and V loads below.
+  // This wave's position: Q^T operand straight from HBM, issued first so it is
+  // in flight together with the K and V loads.
   const int pos = wave;
   const int s = s0 + pos;
-  const bool live = s < S;
+  const bool live = pos < npos;
   const int nqb = (F + 31) / 32;   // query (and key) blocks of 32 frames: 1 or 2
   bf16x8 qreg[2][G::ND];
 #pragma unroll
@@ -81,170 +105,173 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
                                                             (size_t)s * D + d0)
                          : zero_bf16x8();
     }
-  // Zero the pad rows (read by the 32-frame blocks past F of the last position).
-  for (int i = tid; i < kPadRows * G::KS; i += kThreads) {
-    ks[(size_t)kPos * F * G::KS + i] = (bf16)0.f;
-    vs[(size_t)kPos * F * G::KS + i] = (bf16)0.f;
-  }
-  // K, V of positions s0..s0+kPos-1, all frames -> LDS row (pos*F + frame).
-  const int per_frame = kPos * G::CPR;      // 16-byte chunks per frame run
-  const int total = F * per_frame;
-  for (int b0 = 0; b0 < total; b0 += kThreads * kBatch) {
-    uint4 kr[kBatch], vr[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = b0 + u * kThreads + tid;
-      kr[u] = make_uint4(0u, 0u, 0u, 0u);
-      vr[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < total) {
-        const int frame = idx / per_frame, rem = idx % per_frame;
-        const int p = rem / G::CPR, ch = rem % G::CPR;
-        if (s0 + p < S) {
-          const size_t g = base + (size_t)frame * frame_stride + (size_t)(s0 + p) * D + ch * 8;
-          kr[u] = *reinterpret_cast<const uint4*>(K + g);
-          vr[u] = *reinterpret_cast<const uint4*>(V + g);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = b0 + u * kThreads + tid;
-      if (idx < total) {
-        const int frame = idx / per_frame, rem = idx % per_frame;
-        const int p = rem / G::CPR, ch = rem % G::CPR;
-        const size_t l = (size_t)(p * F + frame) * G::KS + ch * 8;
-        *reinterpret_cast<uint4*>(ks + l) = kr[u];
-        *reinterpret_cast<uint4*>(vs + l) = vr[u];
-      }
-    }
-  }
 
+  // K and V runs -> LDS by direct loads.  Slot i of a tensor (16 bytes) is
+  // chunk i % RCH of frame i / RCH; chunks of a missing position re-read the
+  // first position's (finite, never stored).  Load j of the block covers
+  // slots 64 j .. 64 j + 63; the waves take alternate loads, and lanes past
+  // the last slot stay idle.
+  {
+    const int slots = F * G::RCH;
+    const int nj = (slots + kWave - 1) / kWave;
+    const bf16* kb0 = uniform_ptr(K + base + (size_t)s0 * D);
+    const bf16* vb0 = uniform_ptr(V + base + (size_t)s0 * D);
+    const uint32_t k_lds = (uint32_t)(uintptr_t)LDS_PTR(void, ks);
+    const uint32_t v_lds = (uint32_t)(uintptr_t)LDS_PTR(void, vs);
+    const int valid_ch = npos * (D / 8);
+    for (int j = wave; j < nj; j += kWaves) {
+      const int i = j * kWave + lane;
+      const int frame = i / G::RCH, ch = i % G::RCH;
+      const int gch = ch < valid_ch ? ch : ch % (D / 8);
+      const uint32_t off = (uint32_t)(((size_t)frame * frame_stride + gch * 8) * 2);
+      const uint32_t kl = __builtin_amdgcn_readfirstlane(k_lds + (uint32_t)(j * 1024));
+      const uint32_t vl = __builtin_amdgcn_readfirstlane(v_lds + (uint32_t)(j * 1024));
+      if (i < slots) {
+        dma16(kb0, off, kl);
+        dma16(vb0, off, vl);
+      }
+    }
+  }
+  // Runs past F that are read must hold finite values: V runs up to the last
+  // 16-frame PV step (their p are 0), and K runs up to the last 32-frame
+  // block plus one (the d >= D over-read of a row's last 16-wide step reaches
+  // into the next run, against Q's zero padding; scores of frames >= F are
+  // masked after the product).  Zero them.
+  {
+    const int nqb32 = (F + 31) / 32 * 32;
+    const int kpad = min(kMaxF, max(nqb32, F + 1));
+    const int vpad = min(kMaxF, (F + 15) / 16 * 16);
+    for (int i = F * G::RCH + tid; i < kpad * G::RCH; i += kThreads)
+      *reinterpret_cast<uint4*>(ks + i * 8) = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = F * G::RCH + tid; i < vpad * G::RCH; i += kThreads)
+      *reinterpret_cast<uint4*>(vs + i * 8) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0): this wave's loads have landed
   __syncthreads();
 
   if (live) {
-  const bf16* kp = ks + (size_t)pos * F * G::KS;
-  const bf16* vp = vs + (size_t)pos * F * G::KS;
-  const int nsteps = (F + 15) / 16;   // 16-frame PV steps
+    const bf16* kp = ks + pos * D;
+    const bf16* vp = vs + pos * D;
+    const int nsteps = (F + 15) / 16;   // 16-frame PV steps
 
-  // V^T operand for output block nb, PV step t (frames 16t + {h*4+j, 8+h*4+j})
-  // by transposing LDS reads of the row-major V: lane j of a 16-lane group
-  // addresses frame row j/4, columns 4*(j%4)..+3 of a 4x16 block and receives
-  // column j (operand row d = l32).  Operand row D is ones (the softmax
-  // denominator); rows > D are don't-care.
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const bf16* vlane = vp + (h * 4 + (j16 >> 2)) * G::KS + (g16 & 1) * 16 + (j16 & 3) * 4;
-  const bool ones_lane = l32 == (D % 32);
-  const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
-  auto v_operand = [&](int nb, int t) -> bf16x8 {
-    uint4 w;
-    if (nb * 32 < D) {
-      const bf16* p = vlane + t * 16 * G::KS + nb * 32;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::KS));
-      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      w = make_uint4(l2.x, l2.y, h2.x, h2.y);
-      if ((nb + 1) * 32 > D) {
-        w.x = ones_lane ? ones_word : w.x;
-        w.y = ones_lane ? ones_word : w.y;
-        w.z = ones_lane ? ones_word : w.z;
-        w.w = ones_lane ? ones_word : w.w;
+    // V^T operand for output block nb, PV step t (frames 16t + {h*4+j,
+    // 8+h*4+j}) by transposing LDS reads of the frame-major V: lane j of a
+    // 16-lane group addresses frame row j/4, columns 4*(j%4)..+3 of a 4x16
+    // block and receives column j (operand row d = l32).  Operand row D is
+    // ones (the softmax denominator); rows > D are don't-care.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const bf16* vlane = vp + (h * 4 + (j16 >> 2)) * G::RUN + (g16 & 1) * 16 + (j16 & 3) * 4;
+    const bool ones_lane = l32 == (D % 32);
+    const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
+    auto v_operand = [&](int nb, int t) -> bf16x8 {
+      uint4 w;
+      if (nb * 32 < D) {
+        const bf16* p = vlane + t * 16 * G::RUN + nb * 32;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::RUN));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        w = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        if ((nb + 1) * 32 > D) {
+          w.x = ones_lane ? ones_word : w.x;
+          w.y = ones_lane ? ones_word : w.y;
+          w.z = ones_lane ? ones_word : w.z;
+          w.w = ones_lane ? ones_word : w.w;
+        }
+      } else {
+        w = make_uint4(ones_word, ones_word, ones_word, ones_word);
       }
-    } else {
-      w = make_uint4(ones_word, ones_word, ones_word, ones_word);
-    }
-    return __builtin_bit_cast(bf16x8, w);
-  };
+      return __builtin_bit_cast(bf16x8, w);
+    };
 
-  // Phase 1: probabilities of both 32-frame query blocks.  All reads of K
-  // happen here, before any output is staged in the K rows.
-  bf16x8 pbs[2][4];
+    // Phase 1: probabilities of both 32-frame query blocks.  All reads of K
+    // happen here, before any output is staged in the K buffer.
+    bf16x8 pbs[2][4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (qb < nqb) {
-      f32x16 sacc[2];
+    for (int qb = 0; qb < 2; ++qb) {
+      if (qb < nqb) {
+        f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = zero16();
-        if (kb < nqb) {
+        for (int kb = 0; kb < 2; ++kb) {
+          sacc[kb] = zero16();
+          if (kb < nqb) {
 #pragma unroll
-          for (int ds = 0; ds < G::ND; ++ds) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + (size_t)(kb * 32 + l32) * G::KS +
-                                                              ds * 16 + h * 8);
-            sacc[kb] = mfma32(a, qreg[qb][ds], sacc[kb]);
+            for (int ds = 0; ds < G::ND; ++ds) {
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + (kb * 32 + l32) * G::RUN +
+                                                                ds * 16 + h * 8);
+              sacc[kb] = mfma32(a, qreg[qb][ds], sacc[kb]);
+            }
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (kb * 32 + acc_row(r, h) >= F) sacc[kb][r] = -INFINITY;
+            mx = fmaxf(mx, sacc[kb][r]);
+          }
+        mx = max_halves(mx);
+        const float negm = -mx * c;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < nsteps) {
+            const int kb = t >> 1, r0 = (t & 1) * 8;
+            pbs[qb][t] = to_bf16x8(
+                fast_exp2(fmaf(sacc[kb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 1], c, negm)),
+                fast_exp2(fmaf(sacc[kb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 3], c, negm)),
+                fast_exp2(fmaf(sacc[kb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 5], c, negm)),
+                fast_exp2(fmaf(sacc[kb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 7], c, negm)));
           }
         }
       }
-      float mx = -INFINITY;
+    }
+
+    // Phase 2: O^T = V^T P^T per query block, staged frame-major in the K
+    // buffer (this position's columns; the other wave's K reads never touch
+    // them).
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+      if (qb >= nqb) break;
+      f32x16 oacc[G::NB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (kb * 32 + acc_row(r, h) >= F) sacc[kb][r] = -INFINITY;
-          mx = fmaxf(mx, sacc[kb][r]);
-        }
-      mx = max_halves(mx);
-      const float negm = -mx * c;
+      for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = zero16();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t < nsteps) {
-          const int kb = t >> 1, r0 = (t & 1) * 8;
-          pbs[qb][t] = to_bf16x8(
-              fast_exp2(fmaf(sacc[kb][r0 + 0], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 1], c, negm)),
-              fast_exp2(fmaf(sacc[kb][r0 + 2], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 3], c, negm)),
-              fast_exp2(fmaf(sacc[kb][r0 + 4], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 5], c, negm)),
-              fast_exp2(fmaf(sacc[kb][r0 + 6], c, negm)), fast_exp2(fmaf(sacc[kb][r0 + 7], c, negm)));
+#pragma unroll
+          for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = mfma32(v_operand(nb, t), pbs[qb][t], oacc[nb]);
         }
       }
-    }
-  }
-
-  // Phase 2: O^T = V^T P^T per query block, then staged row-major in LDS.
+      const HalfPair pr = half_pair(oacc[G::NBD][G::RD]);
+      const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+      const int frame = qb * 32 + l32;
+      if (frame < F) {
+        bf16* orow = ks + frame * G::RUN + pos * D;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (qb >= nqb) break;
-    f32x16 oacc[G::NB];
+        for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = zero16();
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < nsteps) {
-#pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) oacc[nb] = mfma32(v_operand(nb, t), pbs[qb][t], oacc[nb]);
-      }
-    }
-
-    const HalfPair pr = half_pair(oacc[G::NBD][G::RD]);
-    const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
-    const int frame = qb * 32 + l32;
-    // Stage O row-major in this position's K rows: its own scores are done,
-    // and other waves only read these rows for masked keys or against zero
-    // Q padding, where the values do not matter.
-    if (frame < F) {
-      bf16* orow = ks + (size_t)(pos * F + frame) * G::KS;
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (nb * 32 + g * 8 < D) {  // d0 = nb*32 + g*8 + h*4 < D (D % 8 == 0)
-            const int d0 = nb * 32 + g * 8 + h * 4;
-            const uint2 w = make_uint2(pack_bf16x2(oacc[nb][g * 4 + 0] * inv, oacc[nb][g * 4 + 1] * inv),
-                                       pack_bf16x2(oacc[nb][g * 4 + 2] * inv, oacc[nb][g * 4 + 3] * inv));
-            *reinterpret_cast<uint2*>(orow + d0) = w;
+          for (int g = 0; g < 4; ++g) {
+            if (nb * 32 + g * 8 < D) {  // d0 = nb*32 + g*8 + h*4 < D (D % 8 == 0)
+              const int d0 = nb * 32 + g * 8 + h * 4;
+              const uint2 w = make_uint2(pack_bf16x2(oacc[nb][g * 4 + 0] * inv, oacc[nb][g * 4 + 1] * inv),
+                                         pack_bf16x2(oacc[nb][g * 4 + 2] * inv, oacc[nb][g * 4 + 3] * inv));
+              *reinterpret_cast<uint2*>(orow + d0) = w;
+            }
           }
-        }
+      }
     }
   }
-  }  // live
   __syncthreads();
-  // O of positions s0..s0+kPos-1, all frames: each frame's run of kPos*D elements is
-  // contiguous in HBM, written with 16-byte stores (same pattern as the loads).
-  for (int idx = tid; idx < total; idx += kThreads) {
-    const int frame = idx / per_frame, rem = idx % per_frame;
-    const int p = rem / G::CPR, ch = rem % G::CPR;
-    if (s0 + p < S) {
-      const size_t g = base + (size_t)frame * frame_stride + (size_t)(s0 + p) * D + ch * 8;
-      *reinterpret_cast<uint4*>(O + g) =
-          *reinterpret_cast<const uint4*>(ks + (size_t)(p * F + frame) * G::KS + ch * 8);
+  // O runs back to HBM: run f of the block is contiguous there, written with
+  // 16-byte stores in the order of the loads.
+  {
+    const int valid_ch = npos * (D / 8);
+    bf16* ob0 = O + base + (size_t)s0 * D;
+    for (int i = tid; i < F * G::RCH; i += kThreads) {
+      const int frame = i / G::RCH, ch = i % G::RCH;
+      if (ch < valid_ch)
+        *reinterpret_cast<uint4*>(ob0 + (size_t)frame * frame_stride + ch * 8) =
+            *reinterpret_cast<const uint4*>(ks + i * 8);
     }
   }
 }
@@ -254,14 +281,10 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, int64_
                     float c, hipStream_t stream) {
   const int pos_blocks = (S + kPos - 1) / kPos;
   const int64_t nblocks = nbh * pos_blocks;
-  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const size_t lds = (2 * (size_t)(kPos * F + kPadRows) * Geo<D>::KS + kSlack) * sizeof(bf16);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&temporal_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(temporal_kernel<D>, dim3((unsigned)nblocks), dim3(kThreads), lds, stream,
+  // Direct-load offsets are 32-bit: one (b, h) slab must stay below 4 GiB.
+  if (nblocks > 0x7fffffff || F > kMaxF || (int64_t)F * S * D * 2 >= ((int64_t)1 << 32))
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(temporal_kernel<D>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, F, S, pos_blocks,
                      (int)nblocks, c);
   return hipGetLastError();

@@ -95,6 +95,10 @@ def test_attention_validation_codes():
     assert call(sp, o=A) == lib.PAB_ERR_INVALID_ARG                  # o aliases q
     assert "overlap" in lib.pab_last_error()
     assert call(L.pab_attn_temporal, F=65) == lib.PAB_ERR_UNSUPPORTED
+    # bf16 kernels use 32-bit byte offsets within a sequence / (b, h) slab.
+    assert call(sp, B=1, H=1, F=1, S=1 << 24, D=128) == lib.PAB_ERR_UNSUPPORTED
+    assert call(L.pab_attn_temporal, B=1, H=1, F=64, S=1 << 19, D=64) == lib.PAB_ERR_UNSUPPORTED
+    assert "4 GiB" in lib.pab_last_error()
     cr = L.pab_attn_cross
     assert cr(A, B_, Cc, O, 1, 2, 100, 129, 64, 0, 0.0, None) == lib.PAB_ERR_UNSUPPORTED  # L > 128
     assert cr(A, B_, Cc, O, 1, 2, 0, 16, 64, 0, 0.0, None) == lib.PAB_ERR_INVALID_ARG
