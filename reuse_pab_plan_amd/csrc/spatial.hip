@@ -6,7 +6,9 @@
 //
 // Work split: a 256-thread block owns up to 256 query rows of one sequence,
 // 64 per wave (two 32-row MFMA blocks, so every K and V operand read from LDS
-// feeds two MFMAs; one block per wave for heads wider than 88).  Keys arrive
+// feeds two MFMAs; one block per wave for heads wider than 88).  A sequence's
+// last block, when it holds at most 128 rows, gives each wave one 32-row
+// block instead, so fewer of its waves sit idle.  Keys arrive
 // in 64-row tiles through an LDS ring filled by direct global->LDS loads
 // (global_load_lds_dwordx4): each tile is a whole number of 1 KiB wave-wide
 // loads, dealt round-robin to the waves, issued two tiles ahead (four-stage
@@ -144,7 +146,6 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
                                                              bf16* __restrict__ O, int S, int nqt,
                                                              int nblocks, float c) {
   using G = Geo<D>;
-  constexpr int QB = G::QB;
   __shared__ __attribute__((aligned(16))) bf16 ring[G::NST * G::STAGE];
 
   const int tid = threadIdx.x;
@@ -158,26 +159,6 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   const bf16* __restrict__ Ks = K + base;
   const bf16* __restrict__ Vs = V + base;
   bf16* __restrict__ Os = O + base;
-
-  // This wave's query rows as the B operand (Q^T), resident in registers.
-  const int qrow0 = qt * G::BM + wave * 32 * QB;
-  const bool wave_live = qrow0 < S;
-  bf16x8 qreg[QB][G::ND];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qrow0 + qb * 32 + l32;
-#pragma unroll
-    for (int ds = 0; ds < G::ND; ++ds) {
-      const int d0 = ds * 16 + h * 8;
-      qreg[qb][ds] = (qrow < S && d0 < D)
-                         ? *reinterpret_cast<const bf16x8*>(Qs + (size_t)qrow * D + d0)
-                         : zero_bf16x8();
-    }
-  }
-  // Let Q land before the ring starts: the compiler tracks these loads but
-  // not the direct loads, and would otherwise wait for everything in flight
-  // at the first use of Q inside the loop.
-  wait_vmcnt<0>();
 
   // Direct-load plan of this wave: loads j = wave + 4i.  Load j covers stage
   // slots 64 j .. 64 j + 63; slot s of the K (V) rows is chunk
@@ -246,201 +227,236 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
     if (t + G::NST - 2 < nt) issue(t + G::NST - 2);
   };
 
-  issue(0);
-  if (G::NST == 4 && nt > 1) issue(1);
-
-  if (!wave_live) {
-    // Idle waves still fetch their share of every tile.
-    for (int t = 0; t < nt; ++t) sync_tile(t);
-    return;
-  }
-
-  // Per-lane LDS offsets of the operand reads; the rest of each address is a
-  // compile-time offset.  Transposing V read: lane j of a 16-lane group
-  // addresses row j/4 and columns 4*(j%4)..+3 of a 4x16 block and receives
-  // column j, i.e. V^T row d = l32 of the operand.
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const uint32_t klane = (uint32_t)((l32 * G::KS + h * 8) * 2);
-  const uint32_t vlane = (uint32_t)((G::KREG + (h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 +
-                                     (j16 & 3) * 4) * 2);
-  // Operand row D of V^T (the ones row) lives in lane D % 32 of block D / 32.
-  const bool ones_lane = l32 == (D % 32);
-  const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
-
-  f32x16 oacc[QB][G::NB];
+  // The work of one block for QBX 32-row query blocks per wave.
+  auto run = [&](auto qbx) __attribute__((always_inline)) {
+    constexpr int QBX = decltype(qbx)::value;
+    // This wave's query rows as the B operand (Q^T), resident in registers.
+    const int qrow0 = qt * G::BM + wave * 32 * QBX;
+    const bool wave_live = qrow0 < S;
+    bf16x8 qreg[QBX][G::ND];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QBX; ++qb) {
+      const int qrow = qrow0 + qb * 32 + l32;
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) oacc[qb][nb] = zero16();
-  float mrow[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mrow[qb] = -INFINITY;  // log2 domain (score * c)
-
-  // S^T block of the 32 keys at row kb*32 of the stage whose K rows `kaddr`
-  // points into (per-lane offset included).
-  auto qk = [&](uint32_t kaddr, int kb, f32x16 (&s)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb] = zero16();
-#pragma unroll
-    for (int ds = 0; ds < G::ND; ++ds) {
-      const bf16x8 a = *LDS_PTR(const bf16x8, kaddr + (uint32_t)((kb * 32 * G::KS + ds * 16) * 2));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32(a, qreg[qb][ds], s[qb]);
+      for (int ds = 0; ds < G::ND; ++ds) {
+        const int d0 = ds * 16 + h * 8;
+        qreg[qb][ds] = (qrow < S && d0 < D)
+                           ? *reinterpret_cast<const bf16x8*>(Qs + (size_t)qrow * D + d0)
+                           : zero_bf16x8();
+      }
     }
-  };
-  // Keys >= S do not exist.
-  auto mask = [&](f32x16 (&s)[QB], int key_first) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (key_first + acc_row(r, h) >= S) s[qb][r] = -INFINITY;
-  };
-  auto rowmax = [&](const f32x16 (&s)[QB], float (&mx)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float m = s[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][r]);
-      mx[qb] = max_halves(m);
+    // Let Q land before the ring starts: the compiler tracks these loads but
+    // not the direct loads, and would otherwise wait for everything in flight
+    // at the first use of Q inside the loop.
+    wait_vmcnt<0>();
+
+    issue(0);
+    if (G::NST == 4 && nt > 1) issue(1);
+
+    if (!wave_live) {
+      // Idle waves still fetch their share of every tile.
+      for (int t = 0; t < nt; ++t) sync_tile(t);
+      return;
     }
-  };
-  // Raise the running max where a unit's max exceeds it by more than the
-  // slack, rescaling what has been accumulated so far.
-  auto rescale = [&](const float (&mx)[QB]) __attribute__((always_inline)) {
+
+    // Per-lane LDS offsets of the operand reads; the rest of each address is a
+    // compile-time offset.  Transposing V read: lane j of a 16-lane group
+    // addresses row j/4 and columns 4*(j%4)..+3 of a 4x16 block and receives
+    // column j, i.e. V^T row d = l32 of the operand.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const uint32_t klane = (uint32_t)((l32 * G::KS + h * 8) * 2);
+    const uint32_t vlane = (uint32_t)((G::KREG + (h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 +
+                                       (j16 & 3) * 4) * 2);
+    // Operand row D of V^T (the ones row) lives in lane D % 32 of block D / 32.
+    const bool ones_lane = l32 == (D % 32);
+    const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
+
+    f32x16 oacc[QBX][G::NB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mnew = mx[qb] * c;
-      if (mnew > mrow[qb] + kSlack) {
-        const float alpha = fast_exp2(mrow[qb] - mnew);
+    for (int qb = 0; qb < QBX; ++qb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) oacc[qb][nb] = zero16();
+    float mrow[QBX];
+#pragma unroll
+    for (int qb = 0; qb < QBX; ++qb) mrow[qb] = -INFINITY;  // log2 domain (score * c)
+
+    // S^T block of the 32 keys at row kb*32 of the stage whose K rows `kaddr`
+    // points into (per-lane offset included).
+    auto qk = [&](uint32_t kaddr, int kb, f32x16 (&s)[QBX]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) s[qb] = zero16();
+#pragma unroll
+      for (int ds = 0; ds < G::ND; ++ds) {
+        const bf16x8 a = *LDS_PTR(const bf16x8, kaddr + (uint32_t)((kb * 32 * G::KS + ds * 16) * 2));
+#pragma unroll
+        for (int qb = 0; qb < QBX; ++qb) s[qb] = mfma32(a, qreg[qb][ds], s[qb]);
+      }
+    };
+    // Keys >= S do not exist.
+    auto mask = [&](f32x16 (&s)[QBX], int key_first) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key_first + acc_row(r, h) >= S) s[qb][r] = -INFINITY;
+    };
+    auto rowmax = [&](const f32x16 (&s)[QBX], float (&mx)[QBX]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) {
+        float m = s[qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][r]);
+        mx[qb] = max_halves(m);
+      }
+    };
+    // Raise the running max where a unit's max exceeds it by more than the
+    // slack, rescaling what has been accumulated so far.
+    auto rescale = [&](const float (&mx)[QBX]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) {
+        const float mnew = mx[qb] * c;
+        if (mnew > mrow[qb] + kSlack) {
+          const float alpha = fast_exp2(mrow[qb] - mnew);
+#pragma unroll
+          for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
+          mrow[qb] = mnew;
+        }
+      }
+    };
+    // P^T operand (bf16) of scores r0..r0+7 (r0 = 8*t2): 16 keys per lane half.
+    auto probs = [&](const f32x16 (&s)[QBX], int t2, bf16x8 (&pb)[QBX]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) {
+        const float negm = -mrow[qb];
+        const int r0 = t2 * 8;
+        pb[qb] = to_bf16x8(
+            fast_exp2(fmaf(s[qb][r0 + 0], c, negm)), fast_exp2(fmaf(s[qb][r0 + 1], c, negm)),
+            fast_exp2(fmaf(s[qb][r0 + 2], c, negm)), fast_exp2(fmaf(s[qb][r0 + 3], c, negm)),
+            fast_exp2(fmaf(s[qb][r0 + 4], c, negm)), fast_exp2(fmaf(s[qb][r0 + 5], c, negm)),
+            fast_exp2(fmaf(s[qb][r0 + 6], c, negm)), fast_exp2(fmaf(s[qb][r0 + 7], c, negm)));
+      }
+    };
+    // O^T += V^T P^T over keys kb*32 + 16*t2 .. +15 of the stage whose V rows
+    // `vaddr` points into (per-lane offset included).
+    auto pv = [&](uint32_t vaddr, int kb, int t2, const bf16x8 (&pb)[QBX]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        bf16x8 a;
+        if (nb < G::NB - 1 || G::LAST_READ) {
+          const uint32_t p = vaddr + (uint32_t)(((kb * 32 + t2 * 16) * G::VS + nb * 32) * 2);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
+          a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          if (nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
+            uint4 w = __builtin_bit_cast(uint4, a);
+            w.x = ones_lane ? ones_word : w.x;
+            w.y = ones_lane ? ones_word : w.y;
+            w.z = ones_lane ? ones_word : w.z;
+            w.w = ones_lane ? ones_word : w.w;
+            a = __builtin_bit_cast(bf16x8, w);
+          }
+        } else {
+          a = __builtin_bit_cast(bf16x8, make_uint4(ones_word, ones_word, ones_word, ones_word));
+        }
+#pragma unroll
+        for (int qb = 0; qb < QBX; ++qb) oacc[qb][nb] = mfma32(a, pb[qb], oacc[qb][nb]);
+      }
+    };
+    // One pipelined unit: softmax and PV of the current unit (scores `sc`, V at
+    // row kb_cur*32 of `v_cur`) around the QK of the next unit (K at row
+    // kb_next*32 of `k_next`, scores into `sn`, row maxima into `mxn`).  The
+    // MFMA and VALU streams sit in one basic block, so the scheduler can
+    // interleave them.  With `masked`, keys of the next unit from S on are
+    // masked (only the last tile has such keys).
+    auto unit = [&](auto masked, uint32_t k_next, int kb_next, int key_next, uint32_t v_cur,
+                    int kb_cur, const f32x16 (&sc)[QBX], f32x16 (&sn)[QBX], float (&mxn)[QBX])
+        __attribute__((always_inline)) {
+      bf16x8 p0[QBX], p1[QBX];
+      qk(k_next, kb_next, sn);
+      probs(sc, 0, p0);
+      pv(v_cur, kb_cur, 0, p0);
+      probs(sc, 1, p1);
+      pv(v_cur, kb_cur, 1, p1);
+      if constexpr (decltype(masked)::value) mask(sn, key_next);
+      rowmax(sn, mxn);
+    };
+
+    f32x16 sA[QBX], sB[QBX];
+    float mA[QBX], mB[QBX];
+
+    sync_tile(0);
+    {
+      const uint32_t st = stage_base(0);
+      qk(opaque(st + klane), 0, sA);
+      if (S < 32) mask(sA, 0);
+      rowmax(sA, mA);
+    }
+
+    // One tile per iteration: units 2t (scores in sA) and 2t+1, each with the
+    // QK of the unit after it underneath.  While both of those units have all
+    // 32 keys below S the iteration needs no masking.
+    const int UF = S / 32;   // units with all 32 keys present
+    int t = 0;
+    for (; 2 * t + 2 < UF; ++t) {
+      const uint32_t cur = stage_base(t);
+      const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
+      rescale(mA);
+      unit(std::false_type{}, kc, 1, 0, vc, 0, sA, sB, mB);
+      rescale(mB);
+      sync_tile(t + 1);
+      const uint32_t kn = opaque(stage_base(t + 1) + klane);
+      unit(std::false_type{}, kn, 0, 0, vc, 1, sB, sA, mA);
+    }
+    // The last one or two tiles, masked.  A unit entirely past S (the second
+    // unit of the last tile when S % 64 is 1..32) has all p exactly 0 and
+    // changes nothing; the QK after the last unit runs on stale but in-bounds
+    // LDS and is dropped.
+    for (; t < nt; ++t) {
+      const uint32_t cur = stage_base(t);
+      const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
+      rescale(mA);
+      unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB, mB);
+      rescale(mB);
+      if (t + 1 < nt) sync_tile(t + 1);
+      const uint32_t kn = opaque(stage_base(t + 1) + klane);
+      unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA, mA);
+    }
+
+#pragma unroll
+    for (int qb = 0; qb < QBX; ++qb) {
+      const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
+      const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+      const int qrow = qrow0 + qb * 32 + l32;
+      if (qrow < S) {
+        bf16* orow = Os + (size_t)qrow * D;
 #pragma unroll
         for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
-        mrow[qb] = mnew;
-      }
-    }
-  };
-  // P^T operand (bf16) of scores r0..r0+7 (r0 = 8*t2): 16 keys per lane half.
-  auto probs = [&](const f32x16 (&s)[QB], int t2, bf16x8 (&pb)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float negm = -mrow[qb];
-      const int r0 = t2 * 8;
-      pb[qb] = to_bf16x8(
-          fast_exp2(fmaf(s[qb][r0 + 0], c, negm)), fast_exp2(fmaf(s[qb][r0 + 1], c, negm)),
-          fast_exp2(fmaf(s[qb][r0 + 2], c, negm)), fast_exp2(fmaf(s[qb][r0 + 3], c, negm)),
-          fast_exp2(fmaf(s[qb][r0 + 4], c, negm)), fast_exp2(fmaf(s[qb][r0 + 5], c, negm)),
-          fast_exp2(fmaf(s[qb][r0 + 6], c, negm)), fast_exp2(fmaf(s[qb][r0 + 7], c, negm)));
-    }
-  };
-  // O^T += V^T P^T over keys kb*32 + 16*t2 .. +15 of the stage whose V rows
-  // `vaddr` points into (per-lane offset included).
-  auto pv = [&](uint32_t vaddr, int kb, int t2, const bf16x8 (&pb)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) {
-      bf16x8 a;
-      if (nb < G::NB - 1 || G::LAST_READ) {
-        const uint32_t p = vaddr + (uint32_t)(((kb * 32 + t2 * 16) * G::VS + nb * 32) * 2);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
-        a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        if (nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
-          uint4 w = __builtin_bit_cast(uint4, a);
-          w.x = ones_lane ? ones_word : w.x;
-          w.y = ones_lane ? ones_word : w.y;
-          w.z = ones_lane ? ones_word : w.z;
-          w.w = ones_lane ? ones_word : w.w;
-          a = __builtin_bit_cast(bf16x8, w);
-        }
-      } else {
-        a = __builtin_bit_cast(bf16x8, make_uint4(ones_word, ones_word, ones_word, ones_word));
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma32(a, pb[qb], oacc[qb][nb]);
-    }
-  };
-  // One pipelined unit: softmax and PV of the current unit (scores `sc`, V at
-  // row kb_cur*32 of `v_cur`) around the QK of the next unit (K at row
-  // kb_next*32 of `k_next`, scores into `sn`, row maxima into `mxn`).  The
-  // MFMA and VALU streams sit in one basic block, so the scheduler can
-  // interleave them.  With `masked`, keys of the next unit from S on are
-  // masked (only the last tile has such keys).
-  auto unit = [&](auto masked, uint32_t k_next, int kb_next, int key_next, uint32_t v_cur,
-                  int kb_cur, const f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&mxn)[QB])
-      __attribute__((always_inline)) {
-    bf16x8 p0[QB], p1[QB];
-    qk(k_next, kb_next, sn);
-    probs(sc, 0, p0);
-    pv(v_cur, kb_cur, 0, p0);
-    probs(sc, 1, p1);
-    pv(v_cur, kb_cur, 1, p1);
-    if constexpr (decltype(masked)::value) mask(sn, key_next);
-    rowmax(sn, mxn);
-  };
-
-  f32x16 sA[QB], sB[QB];
-  float mA[QB], mB[QB];
-
-  sync_tile(0);
-  {
-    const uint32_t st = stage_base(0);
-    qk(opaque(st + klane), 0, sA);
-    if (S < 32) mask(sA, 0);
-    rowmax(sA, mA);
-  }
-
-  // One tile per iteration: units 2t (scores in sA) and 2t+1, each with the
-  // QK of the unit after it underneath.  While both of those units have all
-  // 32 keys below S the iteration needs no masking.
-  const int UF = S / 32;   // units with all 32 keys present
-  int t = 0;
-  for (; 2 * t + 2 < UF; ++t) {
-    const uint32_t cur = stage_base(t);
-    const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
-    rescale(mA);
-    unit(std::false_type{}, kc, 1, 0, vc, 0, sA, sB, mB);
-    rescale(mB);
-    sync_tile(t + 1);
-    const uint32_t kn = opaque(stage_base(t + 1) + klane);
-    unit(std::false_type{}, kn, 0, 0, vc, 1, sB, sA, mA);
-  }
-  // The last one or two tiles, masked.  A unit entirely past S (the second
-  // unit of the last tile when S % 64 is 1..32) has all p exactly 0 and
-  // changes nothing; the QK after the last unit runs on stale but in-bounds
-  // LDS and is dropped.
-  for (; t < nt; ++t) {
-    const uint32_t cur = stage_base(t);
-    const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
-    rescale(mA);
-    unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB, mB);
-    rescale(mB);
-    if (t + 1 < nt) sync_tile(t + 1);
-    const uint32_t kn = opaque(stage_base(t + 1) + klane);
-    unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA, mA);
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
-    const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
-    const int qrow = qrow0 + qb * 32 + l32;
-    if (qrow < S) {
-      bf16* orow = Os + (size_t)qrow * D;
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = nb * 32 + g * 8 + h * 4;
-          if (d0 < D) {
-            const uint2 w =
-                make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
-                           pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
-            *reinterpret_cast<uint2*>(orow + d0) = w;
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = nb * 32 + g * 8 + h * 4;
+            if (d0 < D) {
+              const uint2 w =
+                  make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
+                             pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
+              *reinterpret_cast<uint2*>(orow + d0) = w;
+            }
           }
-        }
+      }
+    }
+  };
+
+  // A sequence's last block usually holds fewer rows than the block covers;
+  // when 32 rows per wave cover them, every wave takes one 32-row block
+  // instead of leaving waves idle.
+  if constexpr (G::QB == 2) {
+    if (S - qt * G::BM <= kWaves * 32) {
+      run(std::integral_constant<int, 1>{});
+      return;
     }
   }
+  run(std::integral_constant<int, G::QB>{});
 }
 
 template <int D>

@@ -58,10 +58,11 @@ def to_dev(*ts):
 
 SPATIAL_CASES = [
     # B, H, F, S, D, dtype
-    (1, 2, 3, 300, 72, "bf16"),     # 3 query tiles (ragged), 5 key tiles (ragged)
+    (1, 2, 3, 300, 72, "bf16"),     # last block of 44 rows (one 32-row block per wave), ragged key tiles
     (2, 1, 2, 128, 64, "bf16"),     # exact tiles
     (1, 1, 2, 77, 128, "bf16"),     # widest head
     (1, 3, 1, 200, 8, "bf16"),      # narrowest head (D % 16 == 8)
+    (1, 1, 2, 456, 72, "bf16"),     # last block of 200 rows: two 32-row blocks per wave, one idle wave
     (1, 1, 1, 1000, 120, "bf16"),
     (1, 2, 2, 33, 16, "bf16"),
     (1, 4, 4, 64, 64, "f32"),       # tiny-config shape
