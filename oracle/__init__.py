@@ -20,7 +20,9 @@ Modules:
 
 * ``schedule``   -- which (step, attention type) pairs recompute and which
                     step each reuse takes its output from (pinned: closed-form
-                    counts, brute-force properties, hand-derived tables).
+                    counts, brute-force properties, hand-derived tables), and
+                    the per-type ranges calibrated from a measured attention
+                    difference (pinned: hand-derived cases, invariances).
 * ``attention``  -- softmax(Q K^T * scale) V written out plainly, and the three
                     gathers of it (spatial, temporal, cross) (pinned: row sums,
                     permutation invariance, single key, Q = 0, closed-form
@@ -32,7 +34,13 @@ Modules:
                     identity, recompute count equals the closed form).
 """
 
-from .schedule import in_window, window_bounds, schedule, closed_form_counts  # noqa: F401
+from .schedule import (  # noqa: F401
+    in_window,
+    window_bounds,
+    schedule,
+    closed_form_counts,
+    calibrate_ranges,
+)
 from .attention import (  # noqa: F401
     attn_loop,
     attn_fp64,

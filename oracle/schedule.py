@@ -117,3 +117,65 @@ def closed_form_counts(n_steps: int, ranges, lo_pct: int = 15, hi_pct: int = 85)
     """
     _, w = window_bounds(n_steps, lo_pct, hi_pct)
     return np.array([(n_steps - w) + (w + r) // (r + 1) for r in ranges], dtype=np.int32)
+
+
+def calibrate_ranges(diff, candidates, lo_pct: int = 15, hi_pct: int = 85):
+    """Broadcast ranges per attention type from a measured attention difference.
+
+    What the pages fix: the PAB article ("Implementation") sets each type's
+    broadcast range from how much its attention output changes between
+    consecutive steps in the stable middle -- the less a type changes, the
+    wider its range -- and measures that change by the MSE between the
+    outputs of consecutive steps (Figure 1 caption).  The PAB abstract calls
+    the resulting set of ranges a pyramid chosen by each type's variance.
+
+    Readings where the pages are open (repeated in the design doc):
+
+    5. The change of type a is scored by the plain mean of diff[i][a] over the
+       steps i whose output and predecessor's output both lie in the stable
+       window (i >= 1, in_window(i) and in_window(i - 1)); the sum runs in
+       step order, in fp64.
+    6. The ranges handed out are the caller's candidates, assigned by rank:
+       the type with the largest score gets the smallest candidate, the next
+       largest the next smallest, and so on.  Equal scores rank the lower
+       type index as the larger one.
+
+    Args:
+      diff: [N][T] numbers; diff[i][a] is the MSE between type a's outputs at
+            steps i and i-1 of a trajectory that computes every step (row 0
+            is not used).
+      candidates: T ranges (>= 0) to assign.
+      lo_pct, hi_pct: window edges, as in ``schedule``.
+
+    Returns:
+      (ranges, scores): ranges[a] assigned to type a, and the score of each
+      type (Python floats, i.e. fp64).
+    """
+    n_steps = len(diff)
+    n_types = len(candidates)
+    if n_steps < 1 or n_types < 1:
+        raise ValueError("need at least one step and one type")
+    if any(int(c) < 0 for c in candidates):
+        raise ValueError("candidate ranges must be >= 0")
+    if not (0 <= lo_pct <= hi_pct <= 100):
+        raise ValueError("need 0 <= lo_pct <= hi_pct <= 100")
+    counted = [i for i in range(1, n_steps)
+               if in_window(i, n_steps, lo_pct, hi_pct) and in_window(i - 1, n_steps, lo_pct, hi_pct)]
+    if not counted:
+        raise ValueError("the window holds fewer than two consecutive steps")
+    scores = []
+    for a in range(n_types):
+        total = 0.0
+        for i in counted:
+            d = float(diff[i][a])
+            if not (d >= 0.0) or d == float("inf"):
+                raise ValueError("attention differences must be finite and >= 0")
+            total += d
+        scores.append(total / len(counted))
+    # Most-changing type first; it receives the narrowest range.
+    order = sorted(range(n_types), key=lambda a: (-scores[a], a))
+    ascending = sorted(int(c) for c in candidates)
+    ranges = [0] * n_types
+    for rank, a in enumerate(order):
+        ranges[a] = ascending[rank]
+    return ranges, scores
