@@ -239,6 +239,7 @@ def main():
             raise RuntimeError(f"dispatch mask of type {a} differs from the schedule")
 
     off_ms = None
+    calibration = None
     if args.off_steps > 0:
         torch.cuda.synchronize()
         start.record(stream)
@@ -248,6 +249,16 @@ def main():
         torch.cuda.synchronize()
         off_ms = start.elapsed_time(stop) / args.off_steps
         log(f"PAB off: {off_ms:.3f} ms per trajectory")
+        # Range calibration from the PAB-off trajectory's attention difference.
+        t_cal = time.time()
+        cal_ranges, cal_scores, _ = harness.calibrate(traj_off)
+        calibration = {
+            "candidates": list(cfg.ranges),
+            "ranges": dict(zip(cfg.kinds, map(int, cal_ranges))),
+            "mean_in_window_mse": dict(zip(cfg.kinds, map(float, cal_scores))),
+            "wall_s": time.time() - t_cal,
+        }
+        log(f"calibrated ranges {calibration['ranges']} (configured {dict(zip(cfg.kinds, cfg.ranges))})")
 
     kernels = {}
     for a, kind in enumerate(cfg.kinds):
@@ -310,6 +321,7 @@ def main():
         "pab_on_ms_per_trajectory": on_ms,
         "pab_off_ms_per_trajectory": off_ms,
         "pab_on_with_mse_ms_per_trajectory": drift_ms,
+        "range_calibration": calibration,
         "pab_speedup": (off_ms / on_ms) if off_ms else None,
         "effective_tflops_vs_off_work": flops_off / (on_ms * 1e-3) / 1e12,
         "pab_off_tflops": (flops_off / (off_ms * 1e-3) / 1e12) if off_ms else None,

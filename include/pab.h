@@ -91,6 +91,38 @@ int pab_plan_schedule(int32_t num_steps, int32_t num_types, const int32_t* range
                       int32_t* source_step, int32_t* recompute_count);
 
 /*
+ * pab_plan_calibrate -- broadcast ranges from a measured attention
+ * difference (host only, synchronous).
+ *
+ * PAB article, "Implementation" (each attention type's range is set by how
+ * much its output changes between consecutive steps in the stable middle:
+ * the less it changes, the wider its range) and Figure 1 caption (that
+ * change is the MSE between the outputs of consecutive steps, as computed by
+ * pab_attn_diff_mse); PAB abstract (a pyramid of ranges set by each type's
+ * variance).
+ *
+ * diff[num_steps*num_types] (host, row-major by step): diff[i*num_types+a]
+ * is the attention difference of type a between steps i and i-1 of a
+ * profiling trajectory that computes every step (PAB off); row 0 is not
+ * read.  Counted steps: i >= 1 with both i and i-1 in the window (the
+ * window rule of pab_plan_schedule).  Type a's score is the mean of its
+ * counted differences (fp64, summed in step order).  candidate_ranges[a]
+ * (>= 0) are the ranges to hand out; they are assigned by rank: the type
+ * with the largest score receives the smallest candidate, the next largest
+ * the next smallest, and so on (equal scores: the lower type index ranks as
+ * larger).  ranges_out[num_types] receives the ranges; score_out[num_types]
+ * (may be NULL) the scores.  Values outside the counted steps are never
+ * read.
+ * Errors: PAB_ERR_INVALID_ARG for num_steps < 1, num_types < 1 or > 32,
+ *   NULL diff/candidate_ranges/ranges_out, a negative candidate, not
+ *   0 <= lo <= hi <= 100, a counted difference that is negative, NaN or
+ *   infinite, or a window without two consecutive steps.
+ */
+int pab_plan_calibrate(int32_t num_steps, int32_t num_types, const double* diff,
+                       int32_t window_lo_pct, int32_t window_hi_pct,
+                       const int32_t* candidate_ranges, int32_t* ranges_out, double* score_out);
+
+/*
  * pab_attn_spatial -- attention among the S tokens of each frame.
  *
  * PAB article, "Implementation", second observation (spatial attention).

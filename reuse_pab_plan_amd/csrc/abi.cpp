@@ -31,7 +31,8 @@ bool dims_ok(std::initializer_list<int64_t> dims, int64_t* total) {
 
 bool d_supported(int32_t D) { return D >= 8 && D <= 128 && D % 8 == 0; }
 
-std::string fmt(const char* f, ...) __attribute__((format(printf, 1, 2)));
+}  // namespace
+
 std::string fmt(const char* f, ...) {
   char buf[512];
   va_list ap;
@@ -40,7 +41,6 @@ std::string fmt(const char* f, ...) {
   va_end(ap);
   return buf;
 }
-}  // namespace
 
 int fail(int status, const std::string& msg) {
   g_last_error = msg;

@@ -10,6 +10,7 @@
 
 namespace pab {
 
+std::string fmt(const char* f, ...) __attribute__((format(printf, 1, 2)));  // printf to string
 int fail(int status, const std::string& msg);  // records msg, returns status
 int ok();                                       // clears the error, returns PAB_OK
 int device_error(const char* what, int hip_err);

@@ -268,3 +268,33 @@ class Trajectory:
         """Algorithmic attention flops this trajectory executes."""
         return sum(int(self.counts[a]) * attn_flops(self.cfg, k) * self.cfg.blocks
                    for a, k in enumerate(self.cfg.kinds))
+
+
+# --------------------------------------------------------------- calibration
+
+def calibrate(traj: Trajectory, candidate_ranges=None):
+    """Broadcast ranges from a profiling trajectory's attention difference.
+
+    ``traj`` must be a PAB-off trajectory (every step computes) with inputs
+    attached; it is run once with the attention-difference MSE after every
+    step (the Figure 1 quantity, averaged over blocks), and
+    ``pab_plan_calibrate`` turns the differences into per-type ranges, the
+    candidates (default: the configuration's ranges) handed out by rank.
+    Returns (ranges, scores, diff[N, T]).
+    """
+    import torch
+
+    if traj.pab:
+        raise ValueError("calibration needs a trajectory that computes every step")
+    cfg = traj.cfg
+    keep = traj.drift
+    traj.drift = True
+    try:
+        traj.run(events=False)
+    finally:
+        traj.drift = keep
+    torch.cuda.synchronize(traj.device)
+    diff = traj.drift_out.mean(dim=0).transpose(0, 1).contiguous().cpu().numpy()
+    cand = list(cfg.ranges) if candidate_ranges is None else list(candidate_ranges)
+    ranges, scores = lib.pab_plan_calibrate(diff, cand)
+    return ranges, scores, diff

@@ -33,6 +33,7 @@ KINDS = {"spatial": PAB_SPATIAL, "temporal": PAB_TEMPORAL, "cross": PAB_CROSS}
 # Every symbol include/pab.h declares.
 EXPORTED = (
     "pab_plan_schedule",
+    "pab_plan_calibrate",
     "pab_attn_spatial",
     "pab_attn_temporal",
     "pab_attn_cross",
@@ -99,6 +100,9 @@ def load(path: str = LIB_PATH):
     lib.pab_plan_schedule.argtypes = [i32, i32, C.POINTER(i32), i32, i32,
                                       C.POINTER(C.c_uint8), C.POINTER(i32), C.POINTER(i32)]
     lib.pab_plan_schedule.restype = C.c_int
+    lib.pab_plan_calibrate.argtypes = [i32, i32, C.POINTER(C.c_double), i32, i32,
+                                       C.POINTER(i32), C.POINTER(i32), C.POINTER(C.c_double)]
+    lib.pab_plan_calibrate.restype = C.c_int
     for name in ("pab_attn_spatial", "pab_attn_temporal"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
@@ -150,6 +154,25 @@ def pab_plan_schedule(num_steps: int, ranges, window_lo_pct: int = 15, window_hi
     )
     _check("pab_plan_schedule", st)
     return rec, src, cnt
+
+
+def pab_plan_calibrate(diff, candidate_ranges, window_lo_pct: int = 15, window_hi_pct: int = 85):
+    """diff: [N, T] attention differences (row i: steps i-1 -> i).
+    Returns (ranges int32 [T], scores float64 [T])."""
+    lib = load()
+    d = np.ascontiguousarray(np.asarray(diff, dtype=np.float64))
+    n, t = d.shape
+    c = np.ascontiguousarray(np.asarray(candidate_ranges, dtype=np.int32))
+    if c.shape != (t,):
+        raise ValueError("one candidate range per attention type")
+    out = np.zeros(t, dtype=np.int32)
+    sc = np.zeros(t, dtype=np.float64)
+    st = lib.pab_plan_calibrate(
+        n, t, d.ctypes.data_as(C.POINTER(C.c_double)), window_lo_pct, window_hi_pct,
+        c.ctypes.data_as(C.POINTER(C.c_int32)), out.ctypes.data_as(C.POINTER(C.c_int32)),
+        sc.ctypes.data_as(C.POINTER(C.c_double)))
+    _check("pab_plan_calibrate", st)
+    return out, sc
 
 
 # ---------------------------------------------------------------- device side

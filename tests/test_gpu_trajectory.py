@@ -182,3 +182,36 @@ def test_drift_matches_oracle_mse():
     assert rel.max() <= 1e-6
     # The synthetic workload's U shape: outer steps differ more than inner ones.
     assert got[:, 1].min() > 10 * got[:, 4:8].max()
+
+
+def test_range_calibration_matches_oracle():
+    # PAB article, "Implementation" and Figure 1 caption: ranges follow each
+    # type's consecutive-step attention difference in the stable window.  The
+    # PAB-off tiny trajectory runs on the device with the drift MSE after
+    # every step; the C planner's calibration of those differences must equal
+    # the oracle's calibration of the same numbers bit for bit, and the
+    # oracle's own trajectory (fp64 attention and MSE on the exact inputs the
+    # device consumed) must give the same ranges.
+    _need_gpu()
+    cfg = harness.CONFIGS["tiny"]
+    dev = torch.device("cuda:0")
+    traj = harness.Trajectory(cfg, pab=False, device=dev)
+    traj.inputs = harness.Inputs(cfg, traj.steps_needed(), device=dev)
+    ranges, scores, diff = harness.calibrate(traj)
+    want_r, want_s = oracle.calibrate_ranges(diff.tolist(), list(cfg.ranges))
+    assert list(ranges) == want_r and list(scores) == want_s
+
+    host = lambda t: t.detach().cpu().numpy()
+
+    def inputs_fn(i, a):
+        q, k, v = traj.inputs.get(0, a, i)
+        return {"q": host(q), "k": host(k), "v": host(v)}
+
+    ref = oracle.trajectory(cfg.N, list(cfg.kinds), [0] * len(cfg.kinds), inputs_fn)
+    ref_diff = [[0.0 if d is None else d for d in row] for row in ref["drift"]]
+    ref_r, ref_s = oracle.calibrate_ranges(ref_diff, list(cfg.ranges))
+    rel = np.abs(np.array(scores) - np.array(ref_s)) / np.array(ref_s)
+    print(f"[parity] calibration ranges {list(ranges)} (oracle {ref_r}), "
+          f"scores {list(scores)}, max rel err {rel.max():.2e}", flush=True)
+    assert rel.max() <= 1e-6
+    assert list(ranges) == ref_r
