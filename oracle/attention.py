@@ -109,16 +109,30 @@ def temporal(q, k, v, scale=None):
     return t(attn_fp64(t(q), t(k), t(v), scale))
 
 
-def cross(q, k_text, v_text, scale=None):
+def cross(q, k_text, v_text, scale=None, text_len=None):
     """Video queries against text keys/values.
 
     q: [B,H,F,S,D] or [B,H,Nq,D]; k_text, v_text: [B,H,L,D].
+    text_len: optional per-batch number of real text tokens (1..L); the
+    text tokens past it are padding and take no part (reading of a padded
+    prompt: the video attends to the real tokens of its own prompt only).
     Returns an array shaped like q.
     """
     q = _wide(q)
     shape = q.shape
     qf = q.reshape(shape[0], shape[1], -1, shape[-1])
-    return attn_fp64(qf, k_text, v_text, scale).reshape(shape)
+    if text_len is None:
+        return attn_fp64(qf, k_text, v_text, scale).reshape(shape)
+    if len(text_len) != shape[0]:
+        raise ValueError("one text length per batch entry")
+    out = np.empty(qf.shape, dtype=np.float64)
+    for b, n in enumerate(text_len):
+        n = int(n)
+        if not 1 <= n <= k_text.shape[2]:
+            raise ValueError("text lengths must lie in [1, L]")
+        # Only the first n text tokens of entry b exist for its queries.
+        out[b] = attn_fp64(qf[b], _wide(k_text[b])[:, :n], _wide(v_text[b])[:, :n], scale)
+    return out.reshape(shape)
 
 
 # --------------------------------------------------------------------------
@@ -141,7 +155,9 @@ def temporal_positions(q, k, v, b, h, positions, scale=None):
     return np.swapaxes(attn_fp64(qq, kk, vv, scale), 0, 1)
 
 
-def cross_rows(q_flat, k_text, v_text, b, h, rows, scale=None):
-    """Cross output rows ``rows`` of (b, h); q_flat is [B,H,Nq,D]."""
+def cross_rows(q_flat, k_text, v_text, b, h, rows, scale=None, n_text=None):
+    """Cross output rows ``rows`` of (b, h); q_flat is [B,H,Nq,D].  With
+    ``n_text``, only the first n_text text tokens take part."""
     qq = _wide(q_flat[b, h])[np.asarray(rows)]
-    return attn_fp64(qq, k_text[b, h], v_text[b, h], scale)
+    n = k_text.shape[2] if n_text is None else int(n_text)
+    return attn_fp64(qq, _wide(k_text[b, h])[:n], _wide(v_text[b, h])[:n], scale)

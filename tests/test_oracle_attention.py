@@ -213,3 +213,48 @@ def test_bf16_inputs_widen_exactly():
     o1 = attn_fp64(x, k, v)
     o2 = attn_fp64(x.double().numpy(), k.double().numpy(), v.double().numpy())
     assert np.array_equal(o1, o2)
+
+
+# ------------------------------------------------------------- text padding
+
+def test_cross_text_padding_ignores_pad_tokens():
+    # Padding tokens past an entry's text length take no part: whatever they
+    # hold (here huge values that would dominate any softmax) the output is
+    # the same as with the padding zeroed.
+    q = rnd(2, 2, F, S, D)
+    kt, vt = rnd(2, 2, L, D), rnd(2, 2, L, D)
+    lens = [L - 2, 1]
+    o = cross(q, kt, vt, text_len=lens)
+    k2, v2 = kt.copy(), vt.copy()
+    for b, n in enumerate(lens):
+        k2[b, :, n:] = 1e6
+        v2[b, :, n:] = -1e6
+    assert np.array_equal(cross(q, k2, v2, text_len=lens), o)
+    # One real token: every query returns that token's value row exactly.
+    for h in range(2):
+        assert np.array_equal(o[1, h], np.broadcast_to(vt[1, h, 0], o[1, h].shape))
+    # Full length is the unmasked call.
+    assert np.max(np.abs(cross(q, kt, vt, text_len=[L, L]) - cross(q, kt, vt))) == 0.0
+
+
+def test_cross_text_padding_matches_torch_masked_sdpa():
+    # Library pin: torch CPU fp64 SDPA with a boolean key mask.
+    q = rnd(2, 3, 1, 11, 16)
+    kt, vt = rnd(2, 3, 9, 16), rnd(2, 3, 9, 16)
+    lens = [4, 9]
+    mask = torch.zeros(2, 1, 1, 9, dtype=torch.bool)
+    for b, n in enumerate(lens):
+        mask[b, :, :, :n] = True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.reshape(2, 3, 11, 16)), torch.from_numpy(kt), torch.from_numpy(vt),
+        attn_mask=mask).numpy()
+    got = cross(q, kt, vt, text_len=lens).reshape(2, 3, 11, 16)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_cross_text_padding_rejects_bad_lengths():
+    q = rnd(1, 1, 1, 3, 8)
+    kt, vt = rnd(1, 1, 5, 8), rnd(1, 1, 5, 8)
+    for bad in ([0], [6], [1, 1]):
+        with pytest.raises(ValueError):
+            cross(q, kt, vt, text_len=bad)
