@@ -166,6 +166,23 @@ int pab_attn_cross(const void* q, const void* k_text, const void* v_text, void* 
                    float softmax_scale, void* stream);
 
 /*
+ * pab_attn_cross_masked -- cross attention to padded prompts.
+ *
+ * As pab_attn_cross, but batch entry b has only text_len[b] real text tokens
+ * (1 <= text_len[b] <= L): rows text_len[b]..L-1 of k_text[b,h] and
+ * v_text[b,h] are padding, take no part in the softmax and are never read.
+ * This is how a text encoder's padded prompt reaches cross attention (and
+ * how the two halves of a classifier-free-guidance batch, conditional and
+ * unconditional, differ).  The pages do not discuss masking; the reading is
+ * the usual key-padding mask.  text_len: host array of B int32.
+ * Errors: as pab_attn_cross, plus PAB_ERR_INVALID_ARG for a NULL text_len or
+ * a length outside [1, L].
+ */
+int pab_attn_cross_masked(const void* q, const void* k_text, const void* v_text, void* o,
+                          int32_t B, int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype,
+                          float softmax_scale, const int32_t* text_len, void* stream);
+
+/*
  * pab_mse_workspace_bytes -- device workspace pab_attn_diff_mse needs for
  * n elements (partial sums, one double per reduction block).
  */
@@ -207,6 +224,9 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
  *                two slots), drift[step] = MSE(new output, previous output),
  *                the attention difference of PAB article Figure 1; other
  *                entries are not written.
+ *   text_len     PAB_CROSS only: NULL (all L text tokens real) or a host
+ *                array of B real text-token counts, as for
+ *                pab_attn_cross_masked.
  *
  * pab_step_desc -- the whole block:
  *   num_steps, num_types, recompute  the schedule from pab_plan_schedule
@@ -237,6 +257,7 @@ typedef struct pab_type_desc {
   void* slot[2];
   int32_t B, H, F, S, D, L;
   double* drift;
+  const int32_t* text_len;
 } pab_type_desc;
 
 typedef struct pab_step_desc {

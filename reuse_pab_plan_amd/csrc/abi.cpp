@@ -103,8 +103,9 @@ int check_video_attn(const char* fn, const void* q, const void* k, const void* v
 }
 
 int check_cross_attn(const void* q, const void* kt, const void* vt, const void* o, int32_t B,
-                     int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale) {
-  const char* fn = "pab_attn_cross";
+                     int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale,
+                     const int32_t* text_len) {
+  const char* fn = text_len ? "pab_attn_cross_masked" : "pab_attn_cross";
   if (!q || !kt || !vt || !o) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
   if (!aligned16(q) || !aligned16(kt) || !aligned16(vt) || !aligned16(o))
     return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
@@ -115,6 +116,11 @@ int check_cross_attn(const void* q, const void* kt, const void* vt, const void* 
   int st = check_common(fn, D, dtype, scale);
   if (st) return st;
   if (L > 128) return fail(PAB_ERR_UNSUPPORTED, fmt("%s: L=%d text tokens unsupported (max 128)", fn, L));
+  if (text_len)
+    for (int32_t b = 0; b < B; ++b)
+      if (text_len[b] < 1 || text_len[b] > L)
+        return fail(PAB_ERR_INVALID_ARG,
+                    fmt("%s: text_len[%d]=%d outside [1, L=%d]", fn, b, text_len[b], L));
   if (Nq > ((int64_t)1 << 31) * 32)
     return fail(PAB_ERR_UNSUPPORTED, fmt("%s: Nq too large", fn));
   const size_t es = dtype_size(dtype);
@@ -173,17 +179,36 @@ int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B
 }
 
 int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B, int32_t H,
-              int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale, void* stream) {
+              int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale,
+              const int32_t* text_len, void* stream) {
   const float c = resolve_scale(scale, D);
-  hipError_t e;
-  if (dtype == PAB_BF16) {
-    e = launch_cross_bf16(q, kt, vt, o, (int64_t)B * H, Nq, L, D, c, (hipStream_t)stream);
-  } else {
-    SeqLayout lay{(int64_t)B * H, 1, Nq * D, 0, D, (int64_t)L * D, 0, D, Nq, L};
-    e = launch_attn_f32((const float*)q, (const float*)kt, (const float*)vt, (float*)o, lay, D, c,
-                        (hipStream_t)stream);
+  bool full = true;
+  if (text_len)
+    for (int32_t b = 0; b < B; ++b) full = full && text_len[b] == L;
+  const size_t es = dtype_size(dtype);
+  // All text tokens real: one launch.  Otherwise one launch per batch entry,
+  // each over that entry's real tokens (rows stay L apart in memory).
+  const int32_t parts = full ? 1 : B;
+  for (int32_t b = 0; b < parts; ++b) {
+    const int64_t nbh = full ? (int64_t)B * H : H;
+    const int32_t len = full ? L : text_len[b];
+    const size_t qo = full ? 0 : (size_t)b * H * Nq * D * es;
+    const size_t ko = full ? 0 : (size_t)b * H * L * D * es;
+    const char* qb = (const char*)q + qo;
+    const char* kb = (const char*)kt + ko;
+    const char* vb = (const char*)vt + ko;
+    char* ob = (char*)o + qo;
+    hipError_t e;
+    if (dtype == PAB_BF16) {
+      e = launch_cross_bf16(qb, kb, vb, ob, nbh, Nq, len, L, D, c, (hipStream_t)stream);
+    } else {
+      SeqLayout lay{nbh, 1, Nq * D, 0, D, (int64_t)L * D, 0, D, Nq, len};
+      e = launch_attn_f32((const float*)qb, (const float*)kb, (const float*)vb, (float*)ob, lay, D,
+                          c, (hipStream_t)stream);
+    }
+    if (e != hipSuccess) return device_error("pab_attn_cross launch", e);
   }
-  return e == hipSuccess ? ok() : device_error("pab_attn_cross launch", e);
+  return ok();
 }
 
 int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out, void* ws,
@@ -217,9 +242,18 @@ int pab_attn_temporal(const void* q, const void* k, const void* v, void* o, int3
 int pab_attn_cross(const void* q, const void* k_text, const void* v_text, void* o, int32_t B,
                    int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype,
                    float softmax_scale, void* stream) {
-  int st = check_cross_attn(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale);
+  int st = check_cross_attn(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale, nullptr);
   if (st) return st;
-  return run_cross(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale, stream);
+  return run_cross(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale, nullptr, stream);
+}
+
+int pab_attn_cross_masked(const void* q, const void* k_text, const void* v_text, void* o,
+                          int32_t B, int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype,
+                          float softmax_scale, const int32_t* text_len, void* stream) {
+  if (!text_len) return fail(PAB_ERR_INVALID_ARG, "pab_attn_cross_masked: NULL text_len");
+  int st = check_cross_attn(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale, text_len);
+  if (st) return st;
+  return run_cross(q, k_text, v_text, o, B, H, Nq, L, D, dtype, softmax_scale, text_len, stream);
 }
 
 size_t pab_mse_workspace_bytes(int64_t n) {

@@ -24,8 +24,10 @@ size_t dtype_size(int32_t dtype);
 int check_video_attn(const char* fn, const void* q, const void* k, const void* v, const void* o,
                      int32_t B, int32_t H, int32_t F, int32_t S, int32_t D, int32_t dtype,
                      float scale, bool temporal);
+// text_len: host array of B real text-token counts in [1, L], or NULL (all L).
 int check_cross_attn(const void* q, const void* kt, const void* vt, const void* o, int32_t B,
-                     int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale);
+                     int32_t H, int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale,
+                     const int32_t* text_len);
 int check_mse(const void* a, const void* b, int64_t n, int32_t dtype, const double* out,
               const void* ws, size_t ws_bytes);
 
@@ -35,7 +37,8 @@ int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B,
 int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
                  int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream);
 int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B, int32_t H,
-              int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale, void* stream);
+              int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale,
+              const int32_t* text_len, void* stream);
 int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out, void* ws,
             void* stream);
 

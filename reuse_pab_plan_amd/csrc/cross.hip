@@ -110,7 +110,7 @@ template <int D, int NKB>
 __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restrict__ Q,
                                                            const bf16* __restrict__ Kt,
                                                            const bf16* __restrict__ Vt,
-                                                           bf16* __restrict__ O, int64_t nq, int L,
+                                                           bf16* __restrict__ O, int64_t nq, int L, int Lrows,
                                                            int tiles_per_block, int blocks_per_bh,
                                                            int nblocks, float c) {
   using G = Geo<D, NKB>;
@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
   const int chunk = logical % blocks_per_bh;
   const bf16* __restrict__ Qh = Q + (int64_t)bh * nq * D;
   bf16* __restrict__ Oh = O + (int64_t)bh * nq * D;
-  const bf16* __restrict__ Kh = Kt + (int64_t)bh * L * D;
-  const bf16* __restrict__ Vh = Vt + (int64_t)bh * L * D;
+  // Text rows of (b, h) are Lrows apart; the first L of them are real.
+  const bf16* __restrict__ Kh = Kt + (int64_t)bh * Lrows * D;
+  const bf16* __restrict__ Vh = Vt + (int64_t)bh * Lrows * D;
 
   const int ntiles = (int)((nq + 31) / 32);
   const int t_begin = chunk * tiles_per_block;
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
 
 template <int D, int NKB>
 hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
-                     int64_t nq, int L, float c, hipStream_t stream) {
+                     int64_t nq, int L, int Lrows, float c, hipStream_t stream) {
   // Size the grid to whole waves of resident blocks (2 per CU on 256 CUs),
   // with at most 96 query tiles per block (the K/V load is amortized over
   // them).
@@ -348,28 +349,29 @@ hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int
   const int64_t nblocks = blocks_per_bh * nbh;
   if (nblocks > 0x7fffffff || ntiles > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((cross_kernel<D, NKB>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)kt, (const bf16*)vt, (bf16*)o, nq, L,
+                     (const bf16*)q, (const bf16*)kt, (const bf16*)vt, (bf16*)o, nq, L, Lrows,
                      (int)tiles_per_block, (int)blocks_per_bh, (int)nblocks, c);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* kt, const void* vt, void* o, int64_t nbh, int64_t nq,
-                    int L, float c, hipStream_t stream) {
-  if (L <= 32) return launch_dk<D, 1>(q, kt, vt, o, nbh, nq, L, c, stream);
-  if (L <= 64) return launch_dk<D, 2>(q, kt, vt, o, nbh, nq, L, c, stream);
-  return launch_dk<D, 4>(q, kt, vt, o, nbh, nq, L, c, stream);
+                    int L, int Lrows, float c, hipStream_t stream) {
+  if (L <= 32) return launch_dk<D, 1>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
+  if (L <= 64) return launch_dk<D, 2>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
+  return launch_dk<D, 4>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
 }
 
 }  // namespace
 
 hipError_t launch_cross_bf16(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
-                             int64_t nq, int L, int D, float scale, hipStream_t stream) {
+                             int64_t nq, int L, int Lrows, int D, float scale,
+                             hipStream_t stream) {
   const float c = scale * kLog2e;
   switch (D) {
 #define PAB_CASE(d) \
   case d:           \
-    return launch_d<d>(q, kt, vt, o, nbh, nq, L, c, stream);
+    return launch_d<d>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
     PAB_CASE(8) PAB_CASE(16) PAB_CASE(24) PAB_CASE(32) PAB_CASE(40) PAB_CASE(48) PAB_CASE(56)
     PAB_CASE(64) PAB_CASE(72) PAB_CASE(80) PAB_CASE(88) PAB_CASE(96) PAB_CASE(104) PAB_CASE(112)
     PAB_CASE(120) PAB_CASE(128)

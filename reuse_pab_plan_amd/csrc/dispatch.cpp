@@ -37,7 +37,7 @@ int check_type(const pab_step_desc* d, int a) {
       break;
     case PAB_CROSS:
       st = check_cross_attn(t.q, t.k, t.v, probe_out, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D,
-                            d->dtype, d->softmax_scale);
+                            d->dtype, d->softmax_scale, t.text_len);
       break;
     default:
       return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: unknown attention kind");
@@ -108,7 +108,7 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
         break;
       default:
         st = run_cross(t.q, t.k, t.v, cur, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D, desc->dtype,
-                       desc->softmax_scale, desc->stream);
+                       desc->softmax_scale, t.text_len, desc->stream);
         break;
     }
     if (st) return st;

@@ -25,8 +25,10 @@ hipError_t launch_spatial_bf16(const void* q, const void* k, const void* v, void
                                int S, int D, float scale, hipStream_t stream);
 hipError_t launch_temporal_bf16(const void* q, const void* k, const void* v, void* o, int64_t nbh,
                                 int F, int S, int D, float scale, hipStream_t stream);
+// Text K/V rows of one (b, h) are Lrows apart; the first L of them are real
+// (L <= Lrows, the rest are padding and take no part).
 hipError_t launch_cross_bf16(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
-                             int64_t nq, int L, int D, float scale, hipStream_t stream);
+                             int64_t nq, int L, int Lrows, int D, float scale, hipStream_t stream);
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o,
                            const SeqLayout& lay, int D, float scale, hipStream_t stream);
 

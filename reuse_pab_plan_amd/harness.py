@@ -41,6 +41,11 @@ class Config:
     blocks: int
     seed: int
     desc: str
+    # Real text tokens per batch entry (padded prompts; None = all L real),
+    # and whether the text K/V stay the same at every step (as a real text
+    # encoder's would) instead of following the perturbation model.
+    text_len: tuple | None = None
+    const_text: bool = False
 
     @property
     def video_shape(self):
@@ -71,6 +76,14 @@ CONFIGS = {
     "full3d": Config("full3d", "bf16", 2, 24, 1, 16384, 64, 120, 50, ("spatial", "cross"), (2, 6),
                      1, 5, "full-3D attention, CFG batch 2: 16384 tokens, 24 heads x 64, 120 text "
                      "tokens, 50 steps"),
+    # Padded prompts with classifier-free guidance: the conditional entry has
+    # 77 real text tokens of 120, the unconditional (empty prompt) one; text
+    # K/V constant over the steps.
+    "cfg480": Config("cfg480", "bf16", 2, 16, 48, 1590, 72, 120, 30,
+                     ("spatial", "temporal", "cross"), (2, 4, 6), 1, 6,
+                     "480p-latent block, CFG batch 2 with padded prompts (77 and 1 real text "
+                     "tokens of 120, constant text K/V), 30 steps",
+                     text_len=(77, 1), const_text=True),
 }
 
 TYPE_INDEX = {"spatial": 0, "temporal": 1, "cross": 2}
@@ -79,20 +92,23 @@ TYPE_INDEX = {"spatial": 0, "temporal": 1, "cross": 2}
 # ------------------------------------------------------------ algorithmic work
 
 def attn_flops(cfg: Config, kind: str) -> int:
-    """QK^T and PV multiply-adds (2 flops each) of one call; nothing padded."""
+    """QK^T and PV multiply-adds (2 flops each) of one call; nothing padded
+    (padding text tokens are not work)."""
     B, H, F, S, D, L = cfg.B, cfg.H, cfg.F, cfg.S, cfg.D, cfg.L
     if kind == "spatial":
         return 4 * B * H * F * S * S * D
     if kind == "temporal":
         return 4 * B * H * S * F * F * D
-    return 4 * B * H * F * S * L * D
+    text = sum(cfg.text_len) if cfg.text_len else B * L
+    return 4 * H * F * S * text * D
 
 
 def attn_bytes(cfg: Config, kind: str) -> int:
     """Compulsory HBM bytes of one call: inputs read once, output written once."""
     n = cfg.B * cfg.H * cfg.F * cfg.S * cfg.D * cfg.elem_bytes
     if kind == "cross":
-        return 2 * n + 2 * cfg.B * cfg.H * cfg.L * cfg.D * cfg.elem_bytes
+        text = sum(cfg.text_len) if cfg.text_len else cfg.B * cfg.L
+        return 2 * n + 2 * cfg.H * text * cfg.D * cfg.elem_bytes
     return 4 * n
 
 
@@ -130,10 +146,12 @@ class Inputs:
         qs, kvs = self._shapes(a)
         t = TYPE_INDEX[self.cfg.kinds[a]]
         res = []
+        const = self.cfg.const_text and self.cfg.kinds[a] == "cross"
         for tensor, shape in ((0, qs), (1, kvs), (2, kvs)):
             dst = None if out is None else out[tensor]
             res.append(synth.gpu_tensor(shape, self.cfg.seed, b, t, tensor, i, self.cfg.N,
-                                        self.cfg.dtype, self.device, out=dst))
+                                        self.cfg.dtype, self.device, out=dst,
+                                        perturb=not (const and tensor > 0)))
         return tuple(res)
 
     def get(self, b, a, i):
@@ -176,6 +194,8 @@ class Trajectory:
         # One single-type step descriptor per (block, type), so each type's
         # kernel can be bracketed by events of its own.
         self._rec_cols = [np.ascontiguousarray(self.recompute[:, a]) for a in range(self.T)]
+        self._text_len = (np.ascontiguousarray(np.asarray(cfg.text_len, dtype=np.int32))
+                          if cfg.text_len is not None else None)
         self._descs = []
         self._types = []
         for b in range(cfg.blocks):
@@ -188,6 +208,8 @@ class Trajectory:
                 t[0].B, t[0].H, t[0].F, t[0].S, t[0].D = cfg.video_shape
                 t[0].L = cfg.L if cfg.kinds[a] == "cross" else 0
                 t[0].drift = None
+                if cfg.kinds[a] == "cross" and cfg.text_len is not None:
+                    t[0].text_len = self._text_len.ctypes.data_as(C.POINTER(C.c_int32))
                 d = lib.StepDesc(
                     num_steps=cfg.N, num_types=1,
                     recompute=self._rec_cols[a].ctypes.data_as(C.POINTER(C.c_uint8)),

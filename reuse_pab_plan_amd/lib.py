@@ -37,6 +37,7 @@ EXPORTED = (
     "pab_attn_spatial",
     "pab_attn_temporal",
     "pab_attn_cross",
+    "pab_attn_cross_masked",
     "pab_mse_workspace_bytes",
     "pab_attn_diff_mse",
     "pab_step_dispatch",
@@ -65,6 +66,7 @@ class TypeDesc(C.Structure):
         ("D", C.c_int32),
         ("L", C.c_int32),
         ("drift", C.c_void_p),
+        ("text_len", C.POINTER(C.c_int32)),
     ]
 
 
@@ -109,6 +111,9 @@ def load(path: str = LIB_PATH):
         fn.restype = C.c_int
     lib.pab_attn_cross.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, vp]
     lib.pab_attn_cross.restype = C.c_int
+    lib.pab_attn_cross_masked.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32,
+                                          C.POINTER(i32), vp]
+    lib.pab_attn_cross_masked.restype = C.c_int
     lib.pab_mse_workspace_bytes.argtypes = [i64]
     lib.pab_mse_workspace_bytes.restype = sz
     lib.pab_attn_diff_mse.argtypes = [vp, vp, i64, i32, vp, vp, sz, vp]
@@ -226,6 +231,22 @@ def pab_attn_cross(q, k_text, v_text, o, softmax_scale: float = 0.0, stream=None
     st = load().pab_attn_cross(_ptr(q), _ptr(k_text), _ptr(v_text), _ptr(o), B, H, nq, L, D,
                                _dtype_code(q), softmax_scale, _stream_ptr(stream))
     _check("pab_attn_cross", st)
+    return o
+
+
+def pab_attn_cross_masked(q, k_text, v_text, o, text_len, softmax_scale: float = 0.0, stream=None):
+    """As pab_attn_cross; batch entry b attends to its first text_len[b] text tokens."""
+    B, H = q.shape[0], q.shape[1]
+    D = q.shape[-1]
+    nq = q.numel() // (B * H * D)
+    L = k_text.shape[2]
+    lens = np.ascontiguousarray(np.asarray(text_len, dtype=np.int32))
+    if lens.shape != (B,):
+        raise ValueError("one text length per batch entry")
+    st = load().pab_attn_cross_masked(_ptr(q), _ptr(k_text), _ptr(v_text), _ptr(o), B, H, nq, L, D,
+                                      _dtype_code(q), softmax_scale,
+                                      lens.ctypes.data_as(C.POINTER(C.c_int32)), _stream_ptr(stream))
+    _check("pab_attn_cross_masked", st)
     return o
 
 

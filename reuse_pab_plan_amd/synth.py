@@ -65,10 +65,12 @@ def cpu_tensor(shape, config_seed, block, type_idx, tensor, step, n_steps, dtype
 
 
 def gpu_tensor(shape, config_seed, block, type_idx, tensor, step, n_steps, dtype="bf16",
-               device="cuda", out=None):
+               device="cuda", out=None, perturb=True):
     """One perturbed input tensor generated on the device (torch Philox).
 
     If ``out`` is given the result is written into it (same shape and dtype).
+    With ``perturb=False`` the base tensor alone is returned (the same at
+    every step).
     """
     import torch
 
@@ -76,10 +78,11 @@ def gpu_tensor(shape, config_seed, block, type_idx, tensor, step, n_steps, dtype
     g = torch.Generator(device=device)
     g.manual_seed(stream_id(config_seed, block, type_idx, tensor, -1))
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    g.manual_seed(stream_id(config_seed, block, type_idx, tensor, step))
-    eps = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    x.add_(eps, alpha=step_sigma(step, n_steps))
-    del eps
+    if perturb:
+        g.manual_seed(stream_id(config_seed, block, type_idx, tensor, step))
+        eps = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        x.add_(eps, alpha=step_sigma(step, n_steps))
+        del eps
     if out is None:
         return x.to(tdt)
     out.copy_(x)

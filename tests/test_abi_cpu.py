@@ -100,6 +100,15 @@ def test_attention_validation_codes():
     assert call(L.pab_attn_temporal, B=1, H=1, F=64, S=1 << 19, D=64) == lib.PAB_ERR_UNSUPPORTED
     assert "4 GiB" in lib.pab_last_error()
     cr = L.pab_attn_cross
+    cm = L.pab_attn_cross_masked
+    lens = (C.c_int32 * 2)(5, 16)
+    assert cm(A, B_, Cc, O, 2, 2, 100, 16, 64, 0, 0.0, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert "text_len" in lib.pab_last_error()
+    for bad in ((0, 16), (5, 17), (-1, 3)):
+        lb = (C.c_int32 * 2)(*bad)
+        assert cm(A, B_, Cc, O, 2, 2, 100, 16, 64, 0, 0.0, lb, None) == lib.PAB_ERR_INVALID_ARG
+        assert "outside [1, L" in lib.pab_last_error()
+    assert cm(A, B_, Cc, O, 2, 2, 100, 129, 64, 0, 0.0, lens, None) == lib.PAB_ERR_UNSUPPORTED
     assert cr(A, B_, Cc, O, 1, 2, 100, 129, 64, 0, 0.0, None) == lib.PAB_ERR_UNSUPPORTED  # L > 128
     assert cr(A, B_, Cc, O, 1, 2, 0, 16, 64, 0, 0.0, None) == lib.PAB_ERR_INVALID_ARG
     assert cr(A, B_, Cc, A, 1, 2, 100, 16, 64, 0, 0.0, None) == lib.PAB_ERR_INVALID_ARG

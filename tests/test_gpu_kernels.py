@@ -136,6 +136,40 @@ def test_cross_parity(case):
     assert_close(o, ref, dt, f"cross {case}")
 
 
+MASKED_CROSS_CASES = [
+    # B, H, F, S, L, D, text_len, dtype
+    (2, 2, 2, 100, 120, 72, (77, 1), "bf16"),    # CFG: padded prompt + empty prompt
+    (2, 2, 1, 130, 120, 64, (50, 120), "bf16"),  # no bias column: score masking path
+    (2, 1, 1, 90, 120, 72, (120, 120), "bf16"),  # nothing padded: the single-launch path
+    (3, 1, 1, 70, 33, 8, (33, 2, 17), "bf16"),
+    (2, 4, 4, 64, 16, 64, (16, 5), "f32"),       # tiny-config shape
+]
+
+
+@pytest.mark.parametrize("case", MASKED_CROSS_CASES, ids=lambda c: "x".join(map(str, c[:6])) + "-" + c[7])
+def test_masked_cross_parity(case):
+    # Padded prompts (pab_attn_cross_masked): entry b attends to its first
+    # text_len[b] tokens.  The padding rows are filled with huge values and
+    # NaN on the device: they must not be read.
+    _dev()
+    B, H, F, S, L, D, lens, dt = case
+    print(f"[case] masked cross {case}", flush=True)
+    q, k, v = inputs((B, H, F, S, D), dt, 29, 2, kv_shape=(B, H, L, D))
+    ref = oracle.cross(q, k, v, text_len=lens)
+    qd, kd, vd = to_dev(q, k, v)
+    for b, n in enumerate(lens):
+        kd[b, :, n:] = float("nan")
+        vd[b, :, n:] = 1e30
+    o = torch.empty_like(qd)
+    lib.pab_attn_cross_masked(qd, kd, vd, o, lens)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    assert_close(o, ref, dt, f"masked cross {case}")
+    for b, n in enumerate(lens):
+        if n == 1:  # a single real text token returns its value row exactly
+            assert torch.equal(o[b], vd[b, :, :1, None, :].expand_as(o[b]))
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_single_key_returns_v_bitwise(dt):
     _dev()

@@ -51,9 +51,23 @@ def _sample_check(cfg, kind, q, k, v, out, label):
     else:
         nq = F * S
         rows = np.arange(0, nq, max(1, nq // 1000))
+        n_text = cfg.text_len[0] if cfg.text_len else None
         ref = oracle.cross_rows(host(q.view(B, H, nq, D)[0, 1][None, None]),
-                                host(k[0, 1][None, None]), host(v[0, 1][None, None]), 0, 0, rows)
+                                host(k[0, 1][None, None]), host(v[0, 1][None, None]), 0, 0, rows,
+                                n_text=n_text)
         got = host(out.view(B, H, nq, D)[0, 1])[rows]
+        if cfg.text_len:
+            # Every other entry, sampled too (its own number of text tokens).
+            for b in range(1, B):
+                rb = oracle.cross_rows(host(q.view(B, H, nq, D)[b, 0][None, None]),
+                                       host(k[b, 0][None, None]), host(v[b, 0][None, None]), 0, 0,
+                                       rows, n_text=cfg.text_len[b])
+                gb = host(out.view(B, H, nq, D)[b, 0])[rows]
+                eb = gb - rb
+                mxb = float(np.abs(eb).max())
+                rlb = float(np.linalg.norm(eb) / np.linalg.norm(rb))
+                print(f"[parity] {label} entry {b}: max_abs={mxb:.2e} rel_l2={rlb:.2e}", flush=True)
+                assert mxb <= 2e-2 and rlb <= 5e-3, (label, b, mxb, rlb)
     err = got - ref
     mx, rl = float(np.abs(err).max()), float(np.linalg.norm(err) / np.linalg.norm(ref))
     tol = (2e-2, 5e-3) if cfg.dtype == "bf16" else (1e-5, 1e-5)
@@ -122,6 +136,13 @@ def test_b480_trajectory():
 def test_full3d_trajectory():
     _need_gpu()
     _run_checked(harness.CONFIGS["full3d"], check_steps=(8,))
+
+
+def test_cfg480_padded_prompts_trajectory():
+    # CFG batch with padded prompts (77 and 1 real text tokens of 120) and
+    # constant text K/V, through the dispatcher's per-type text lengths.
+    _need_gpu()
+    _run_checked(harness.CONFIGS["cfg480"])
 
 
 def test_stack28_cache_first_steps():
