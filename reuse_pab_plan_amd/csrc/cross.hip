@@ -334,16 +334,24 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
 template <int D, int NKB>
 hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
                      int64_t nq, int L, int Lrows, float c, hipStream_t stream) {
-  // Size the grid to whole waves of resident blocks (2 per CU on 256 CUs),
-  // with at most 96 query tiles per block (the K/V load is amortized over
-  // them).
+  // Size the grid to whole waves of resident blocks (as many per CU as the
+  // LDS allows, at most 2, on 256 CUs): each (b, h) gets the same number of
+  // blocks, as many as keep the grid within the fewest waves that leave at
+  // most 96 query tiles per block (the text K/V load is amortized over them).
+  using G = Geo<D, NKB>;
+  constexpr int kLdsBytes = (G::KROWS * G::KS + G::VROWS * G::VS + G::VSLACK) * 2 +
+                            kWaves * 2 * G::QSTAGE * 2;
+  constexpr int kPerCu = (160 * 1024) / kLdsBytes >= 2 ? 2 : 1;
   const int64_t ntiles = (nq + 31) / 32;
-  const int64_t total = ntiles * nbh;
-  const int64_t wave_blocks = 512;
-  int64_t target = ((total + wave_blocks * 96 - 1) / (wave_blocks * 96)) * wave_blocks;
-  int64_t blocks_per_bh = (target + nbh - 1) / nbh;
+  const int64_t wave_blocks = 256 * kPerCu;
+  int64_t blocks_per_bh = 1;
+  if (nbh < wave_blocks) {
+    for (int64_t m = 1;; ++m) {
+      blocks_per_bh = (m * wave_blocks) / nbh;
+      if (blocks_per_bh >= ntiles || (ntiles + blocks_per_bh - 1) / blocks_per_bh <= 96) break;
+    }
+  }
   if (blocks_per_bh > ntiles) blocks_per_bh = ntiles;
-  if (blocks_per_bh < 1) blocks_per_bh = 1;
   const int64_t tiles_per_block = (ntiles + blocks_per_bh - 1) / blocks_per_bh;
   blocks_per_bh = (ntiles + tiles_per_block - 1) / tiles_per_block;
   const int64_t nblocks = blocks_per_bh * nbh;
