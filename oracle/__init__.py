@@ -29,6 +29,10 @@ Modules:
                     two-key case, literal loops, torch CPU fp64 SDPA).
 * ``mse``        -- mean squared difference of two attention outputs (pinned:
                     hand example, identities, exact dyadic shifts).
+* ``projection`` -- the input (q/k/v) and output projections around an
+                    attention, in head-major layout (pinned: identity
+                    weights, exact small integers, torch CPU fp64 linear,
+                    head relabelling).
 * ``trajectory`` -- the broadcast cache run over a whole denoising trajectory
                     (pinned: PAB-off equals per-step attention, reuse is
                     identity, recompute count equals the closed form).
@@ -53,4 +57,5 @@ from .attention import (  # noqa: F401
     cross_rows,
 )
 from .mse import mse  # noqa: F401
+from .projection import linear, proj_in, proj_out  # noqa: F401
 from .trajectory import trajectory  # noqa: F401
