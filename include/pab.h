@@ -183,6 +183,37 @@ int pab_attn_cross_masked(const void* q, const void* k_text, const void* v_text,
                           float softmax_scale, const int32_t* text_len, void* stream);
 
 /*
+ * pab_proj_in -- input projection of an attention module (bf16).
+ *
+ * PAB article, "Implementation": a broadcast step reuses the attention
+ * module's output, so on such a step this projection is skipped with the
+ * attention.  y = x w^T for the F*S tokens of each batch entry, written as
+ * n_out head-major tensors: x is token-major [B, F*S, C] with C = H*D (token
+ * f*S + s); w is a linear layer's weight [n_out*C, C] (out_features x
+ * in_features); output feature j goes to tensor j / C (out0, out1, out2),
+ * head (j % C) / D, channel j % D, i.e. out_i is [B, H, F, S, D], the layout
+ * of the attention calls.  n_out = 3 gives q, k, v; 2 gives k, v (e.g. of the
+ * text tokens: F = 1, S = L); 1 gives q.  fp32 accumulation.
+ * Supported: bf16 only (else PAB_ERR_UNSUPPORTED), D as for the attention
+ * calls, C a multiple of 32 and <= 16384, every tensor under 4 GiB.
+ * Outputs must not overlap each other or the inputs.
+ */
+int pab_proj_in(const void* x, const void* w, void* out0, void* out1, void* out2, int32_t n_out,
+                int32_t B, int32_t F, int32_t S, int32_t H, int32_t D, int32_t dtype,
+                void* stream);
+
+/*
+ * pab_proj_out -- output projection of an attention module (bf16).
+ *
+ * Same passage as pab_proj_in.  y = o' w^T where o' is the head-major
+ * attention output o [B, H, F, S, D] read token by token (input feature
+ * h*D + d) and w is [C, C]; y is token-major [B, F*S, C].  Same support and
+ * error rules as pab_proj_in.
+ */
+int pab_proj_out(const void* o, const void* w, void* y, int32_t B, int32_t F, int32_t S,
+                 int32_t H, int32_t D, int32_t dtype, void* stream);
+
+/*
  * pab_mse_workspace_bytes -- device workspace pab_attn_diff_mse needs for
  * n elements (partial sums, one double per reduction block).
  */

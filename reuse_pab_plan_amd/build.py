@@ -32,6 +32,7 @@ SOURCES = [
     "spatial.hip",
     "cross.hip",
     "temporal.hip",
+    "proj.hip",
 ]
 
 # Packed fp32 instructions are disabled for all device code on purpose.

@@ -32,6 +32,14 @@ hipError_t launch_cross_bf16(const void* q, const void* kt, const void* vt, void
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o,
                            const SeqLayout& lay, int D, float scale, hipStream_t stream);
 
+// Projections around an attention (bf16): Y = X W^T with W [N, K].  gather:
+// X is a head-major attention output [B, H, T, D] (k = h*D + d); scatter: Y
+// goes to out[0..N/(H*D)-1] as head-major tensors [B, H, T, D]; otherwise X
+// is token-major [M, K] and Y is out[0] token-major [M, N].
+hipError_t launch_proj_bf16(const void* x, const void* w, void* const out[3], int64_t M, int N,
+                            int K, int T, int H, int D, bool gather, bool scatter,
+                            hipStream_t stream);
+
 int mse_num_blocks(int64_t n, int dtype);
 hipError_t launch_mse(const void* a, const void* b, int64_t n, int dtype, double* out,
                       double* partials, hipStream_t stream);

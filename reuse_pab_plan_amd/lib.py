@@ -38,6 +38,8 @@ EXPORTED = (
     "pab_attn_temporal",
     "pab_attn_cross",
     "pab_attn_cross_masked",
+    "pab_proj_in",
+    "pab_proj_out",
     "pab_mse_workspace_bytes",
     "pab_attn_diff_mse",
     "pab_step_dispatch",
@@ -114,6 +116,10 @@ def load(path: str = LIB_PATH):
     lib.pab_attn_cross_masked.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32,
                                           C.POINTER(i32), vp]
     lib.pab_attn_cross_masked.restype = C.c_int
+    lib.pab_proj_in.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pab_proj_in.restype = C.c_int
+    lib.pab_proj_out.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pab_proj_out.restype = C.c_int
     lib.pab_mse_workspace_bytes.argtypes = [i64]
     lib.pab_mse_workspace_bytes.restype = sz
     lib.pab_attn_diff_mse.argtypes = [vp, vp, i64, i32, vp, vp, sz, vp]
@@ -248,6 +254,25 @@ def pab_attn_cross_masked(q, k_text, v_text, o, text_len, softmax_scale: float =
                                       lens.ctypes.data_as(C.POINTER(C.c_int32)), _stream_ptr(stream))
     _check("pab_attn_cross_masked", st)
     return o
+
+
+def pab_proj_in(x, w, outs, frames: int, tokens: int, heads: int, head_dim: int, stream=None):
+    """x: [B, F*S, C] token-major; w: [n*C, C]; outs: n head-major tensors [B, H, F, S, D]."""
+    n = len(outs)
+    ptrs = [_ptr(t) for t in outs] + [None] * (3 - n)
+    st = load().pab_proj_in(_ptr(x), _ptr(w), ptrs[0], ptrs[1], ptrs[2], n, x.shape[0], frames,
+                            tokens, heads, head_dim, _dtype_code(x), _stream_ptr(stream))
+    _check("pab_proj_in", st)
+    return outs
+
+
+def pab_proj_out(o, w, y, stream=None):
+    """o: [B, H, F, S, D] head-major; w: [C, C]; y: [B, F*S, C] token-major."""
+    B, H, F, S, D = o.shape
+    st = load().pab_proj_out(_ptr(o), _ptr(w), _ptr(y), B, F, S, H, D, _dtype_code(o),
+                             _stream_ptr(stream))
+    _check("pab_proj_out", st)
+    return y
 
 
 def pab_mse_workspace_bytes(n: int) -> int:
