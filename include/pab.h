@@ -258,6 +258,22 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
  *   text_len     PAB_CROSS only: NULL (all L text tokens real) or a host
  *                array of B real text-token counts, as for
  *                pab_attn_cross_masked.
+ *   x ... scratch  the attention module (optional; x = NULL: attention
+ *                only).  With x set (bf16 only), a recompute runs the whole
+ *                module -- input projection, attention, output projection --
+ *                and the slot holds the module output, so a broadcast step
+ *                skips all three (PAB article, "Implementation").  q, k, v
+ *                are then not read.
+ *       x        module input, token-major [B, F*S, C], C = H*D
+ *       x_text   PAB_CROSS: text tokens [B, L, C] (key/value projection)
+ *       w_in     [3C, C] q/k/v projection (self types); PAB_CROSS: [C, C]
+ *                query projection
+ *       w_kv     PAB_CROSS: [2C, C] key/value projection of the text
+ *       w_out    [C, C] output projection
+ *       scratch  device buffers for q, k, v and the attention output, in the
+ *                attention layout ([B,H,F,S,D]; PAB_CROSS k, v: [B,H,L,D]);
+ *                contents are overwritten
+ *                Slots then hold [B, F*S, C] (the same size as O).
  *
  * pab_step_desc -- the whole block:
  *   num_steps, num_types, recompute  the schedule from pab_plan_schedule
@@ -289,6 +305,12 @@ typedef struct pab_type_desc {
   int32_t B, H, F, S, D, L;
   double* drift;
   const int32_t* text_len;
+  const void* x;
+  const void* x_text;
+  const void* w_in;
+  const void* w_kv;
+  const void* w_out;
+  void* scratch[4];
 } pab_type_desc;
 
 typedef struct pab_step_desc {

@@ -57,5 +57,5 @@ from .attention import (  # noqa: F401
     cross_rows,
 )
 from .mse import mse  # noqa: F401
-from .projection import linear, proj_in, proj_out  # noqa: F401
+from .projection import linear, proj_in, proj_out, module  # noqa: F401
 from .trajectory import trajectory  # noqa: F401

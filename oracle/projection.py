@@ -60,3 +60,25 @@ def proj_out(o, w):
     b, h, f, s, d = o.shape
     tokens = o.transpose(0, 2, 3, 1, 4).reshape(b, f * s, h * d)
     return linear(tokens, w)
+
+
+def module(kind: str, x, w_in, w_out, n_heads: int, head_dim: int, frames: int, tokens: int,
+           x_text=None, w_kv=None, text_len=None, scale=None):
+    """One attention module: input projection, attention, output projection.
+
+    kind: "spatial" / "temporal" / "cross".  x: [B, F*S, C]; w_in: [3C, C]
+    (cross: [C, C], the query projection, with w_kv [2C, C] projecting the
+    text tokens x_text [B, L, C]); w_out: [C, C].  Returns [B, F*S, C].
+    """
+    from . import attention as _attn
+
+    if kind == "cross":
+        (q,) = proj_in(x, w_in, n_heads, head_dim, frames, tokens)
+        xt = _wide(x_text)
+        k, v = proj_in(xt, w_kv, n_heads, head_dim, 1, xt.shape[1])
+        o = _attn.cross(q, k[:, :, 0], v[:, :, 0], scale, text_len=text_len)
+    else:
+        q, k, v = proj_in(x, w_in, n_heads, head_dim, frames, tokens)
+        fn = _attn.spatial if kind == "spatial" else _attn.temporal
+        o = fn(q, k, v, scale)
+    return proj_out(o, w_out)

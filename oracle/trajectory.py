@@ -21,7 +21,7 @@ _KERNELS = {
 }
 
 
-def trajectory(n_steps, kinds, ranges, inputs_fn, lo_pct=15, hi_pct=85):
+def trajectory(n_steps, kinds, ranges, inputs_fn, lo_pct=15, hi_pct=85, compute=None):
     """Run the cache.
 
     Args:
@@ -30,6 +30,8 @@ def trajectory(n_steps, kinds, ranges, inputs_fn, lo_pct=15, hi_pct=85):
       ranges:  broadcast range per type.
       inputs_fn(step, type_index) -> dict with "q", "k", "v" (and optional
                "scale"); called only where the schedule recomputes.
+      compute: optional function (kind, inputs) -> output replacing the
+               attention (e.g. a whole attention module).
 
     Returns a dict with
       "outputs":   outputs[i][a], the attention output of step i, type a
@@ -49,7 +51,8 @@ def trajectory(n_steps, kinds, ranges, inputs_fn, lo_pct=15, hi_pct=85):
         row, drow = [], []
         for a, kind in enumerate(kinds):
             if recompute[i, a]:
-                out = _KERNELS[kind](inputs_fn(i, a))
+                x = inputs_fn(i, a)
+                out = compute(kind, x) if compute is not None else _KERNELS[kind](x)
                 calls += 1
                 drow.append(None if cache[a] is None else _mse(out, cache[a]))
                 cache[a] = out

@@ -217,6 +217,58 @@ int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out,
   return e == hipSuccess ? ok() : device_error("pab_attn_diff_mse launch", e);
 }
 
+
+int check_proj(const char* fn, const void* x, const void* w, void* const outs[3], int32_t n_out,
+               int32_t B, int32_t F, int32_t S, int32_t H, int32_t D, int32_t dtype, bool in) {
+  if (!x || !w) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
+  if (n_out < 1 || n_out > 3)
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: n_out must be 1, 2 or 3", fn));
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i] || !aligned16(outs[i]))
+      return fail(PAB_ERR_INVALID_ARG, fmt("%s: output %d NULL or not 16-byte aligned", fn, i));
+  if (!aligned16(x) || !aligned16(w))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
+  int64_t n = 0;
+  if (!dims_ok({B, H, F, S, D}, &n))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: bad shape B=%d H=%d F=%d S=%d D=%d", fn, B, H, F, S, D));
+  if (dtype != PAB_BF16)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: only bf16 projections are built", fn));
+  if (!d_supported(D)) return fail(PAB_ERR_UNSUPPORTED, fmt("%s: head dim D=%d unsupported", fn, D));
+  const int64_t C = (int64_t)H * D;
+  if (C % 32 != 0 || C > 16384)
+    return fail(PAB_ERR_UNSUPPORTED,
+                fmt("%s: hidden size H*D=%lld must be a multiple of 32, <= 16384", fn, (long long)C));
+  const size_t bytes = (size_t)n * 2;
+  if (bytes >= ((size_t)1 << 32))
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: tensors of 4 GiB or more are not supported", fn));
+  const size_t wbytes = (size_t)(in ? n_out : 1) * C * C * 2;
+  for (int i = 0; i < n_out; ++i) {
+    if (ranges_overlap(outs[i], bytes, x, bytes) || ranges_overlap(outs[i], bytes, w, wbytes))
+      return fail(PAB_ERR_INVALID_ARG, fmt("%s: output %d overlaps an input", fn, i));
+    for (int j = 0; j < i; ++j)
+      if (ranges_overlap(outs[i], bytes, outs[j], bytes))
+        return fail(PAB_ERR_INVALID_ARG, fmt("%s: outputs %d and %d overlap", fn, j, i));
+  }
+  return PAB_OK;
+}
+
+int run_proj_in(const void* x, const void* w, void* const outs[3], int32_t n_out, int32_t B,
+                int32_t F, int32_t S, int32_t H, int32_t D, void* stream) {
+  const int64_t C = (int64_t)H * D, T = (int64_t)F * S;
+  void* o3[3] = {outs[0], n_out > 1 ? outs[1] : nullptr, n_out > 2 ? outs[2] : nullptr};
+  hipError_t e = launch_proj_bf16(x, w, o3, (int64_t)B * T, (int)(n_out * C), (int)C, (int)T, H,
+                                  D, false, true, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : device_error("pab_proj_in launch", e);
+}
+
+int run_proj_out(const void* o, const void* w, void* y, int32_t B, int32_t F, int32_t S, int32_t H,
+                 int32_t D, void* stream) {
+  const int64_t C = (int64_t)H * D, T = (int64_t)F * S;
+  void* outs[3] = {y, nullptr, nullptr};
+  hipError_t e = launch_proj_bf16(o, w, outs, (int64_t)B * T, (int)C, (int)C, (int)T, H, D, true,
+                                  false, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : device_error("pab_proj_out launch", e);
+}
 }  // namespace pab
 
 using namespace pab;
@@ -259,67 +311,18 @@ int pab_attn_cross_masked(const void* q, const void* k_text, const void* v_text,
 int pab_proj_in(const void* x, const void* w, void* out0, void* out1, void* out2, int32_t n_out,
                 int32_t B, int32_t F, int32_t S, int32_t H, int32_t D, int32_t dtype,
                 void* stream) {
-  const char* fn = "pab_proj_in";
   void* outs[3] = {out0, out1, out2};
-  if (!x || !w) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
-  if (n_out < 1 || n_out > 3)
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: n_out must be 1, 2 or 3", fn));
-  for (int i = 0; i < n_out; ++i)
-    if (!outs[i] || !aligned16(outs[i]))
-      return fail(PAB_ERR_INVALID_ARG, fmt("%s: output %d NULL or not 16-byte aligned", fn, i));
-  if (!aligned16(x) || !aligned16(w))
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
-  int64_t n = 0;
-  if (!dims_ok({B, H, F, S, D}, &n))
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: bad shape B=%d H=%d F=%d S=%d D=%d", fn, B, H, F, S, D));
-  if (dtype != PAB_BF16)
-    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: only bf16 projections are built", fn));
-  if (!d_supported(D)) return fail(PAB_ERR_UNSUPPORTED, fmt("%s: head dim D=%d unsupported", fn, D));
-  const int64_t C = (int64_t)H * D;
-  if (C % 32 != 0 || C > 16384)
-    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: hidden size H*D=%lld must be a multiple of 32, <= 16384", fn, (long long)C));
-  const size_t bytes = (size_t)n * 2;
-  if (bytes >= ((size_t)1 << 32))
-    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: tensors of 4 GiB or more are not supported", fn));
-  for (int i = 0; i < n_out; ++i) {
-    if (ranges_overlap(outs[i], bytes, x, bytes) ||
-        ranges_overlap(outs[i], bytes, w, (size_t)n_out * C * C * 2))
-      return fail(PAB_ERR_INVALID_ARG, fmt("%s: output %d overlaps an input", fn, i));
-    for (int j = 0; j < i; ++j)
-      if (ranges_overlap(outs[i], bytes, outs[j], bytes))
-        return fail(PAB_ERR_INVALID_ARG, fmt("%s: outputs %d and %d overlap", fn, j, i));
-  }
-  const int64_t T = (int64_t)F * S;
-  hipError_t e = launch_proj_bf16(x, w, outs, (int64_t)B * T, (int)(n_out * C), (int)C, (int)T, H,
-                                  D, false, true, (hipStream_t)stream);
-  return e == hipSuccess ? ok() : device_error("pab_proj_in launch", e);
+  int st = check_proj("pab_proj_in", x, w, outs, n_out, B, F, S, H, D, dtype, true);
+  if (st) return st;
+  return run_proj_in(x, w, outs, n_out, B, F, S, H, D, stream);
 }
 
 int pab_proj_out(const void* o, const void* w, void* y, int32_t B, int32_t F, int32_t S,
                  int32_t H, int32_t D, int32_t dtype, void* stream) {
-  const char* fn = "pab_proj_out";
-  if (!o || !w || !y) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
-  if (!aligned16(o) || !aligned16(w) || !aligned16(y))
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
-  int64_t n = 0;
-  if (!dims_ok({B, H, F, S, D}, &n))
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: bad shape B=%d H=%d F=%d S=%d D=%d", fn, B, H, F, S, D));
-  if (dtype != PAB_BF16)
-    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: only bf16 projections are built", fn));
-  if (!d_supported(D)) return fail(PAB_ERR_UNSUPPORTED, fmt("%s: head dim D=%d unsupported", fn, D));
-  const int64_t C = (int64_t)H * D;
-  if (C % 32 != 0 || C > 16384)
-    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: hidden size H*D=%lld must be a multiple of 32, <= 16384", fn, (long long)C));
-  const size_t bytes = (size_t)n * 2;
-  if (bytes >= ((size_t)1 << 32))
-    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: tensors of 4 GiB or more are not supported", fn));
-  if (ranges_overlap(y, bytes, o, bytes) || ranges_overlap(y, bytes, w, (size_t)C * C * 2))
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: output overlaps an input", fn));
-  const int64_t T = (int64_t)F * S;
   void* outs[3] = {y, nullptr, nullptr};
-  hipError_t e = launch_proj_bf16(o, w, outs, (int64_t)B * T, (int)C, (int)C, (int)T, H, D, true,
-                                  false, (hipStream_t)stream);
-  return e == hipSuccess ? ok() : device_error("pab_proj_out launch", e);
+  int st = check_proj("pab_proj_out", o, w, outs, 1, B, F, S, H, D, dtype, false);
+  if (st) return st;
+  return run_proj_out(o, w, y, B, F, S, H, D, stream);
 }
 
 size_t pab_mse_workspace_bytes(int64_t n) {

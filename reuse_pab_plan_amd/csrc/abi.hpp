@@ -42,4 +42,14 @@ int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B,
 int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out, void* ws,
             void* stream);
 
+// Projections around an attention (bf16).  in = true: input projection
+// (x token-major [B, F*S, C] -> n_out head-major tensors); false: output
+// projection (head-major x -> outs[0] token-major).
+int check_proj(const char* fn, const void* x, const void* w, void* const outs[3], int32_t n_out,
+               int32_t B, int32_t F, int32_t S, int32_t H, int32_t D, int32_t dtype, bool in);
+int run_proj_in(const void* x, const void* w, void* const outs[3], int32_t n_out, int32_t B,
+                int32_t F, int32_t S, int32_t H, int32_t D, void* stream);
+int run_proj_out(const void* o, const void* w, void* y, int32_t B, int32_t F, int32_t S, int32_t H,
+                 int32_t D, void* stream);
+
 }  // namespace pab

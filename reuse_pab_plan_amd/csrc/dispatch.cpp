@@ -9,7 +9,9 @@
 // output survives the recompute, so the attention difference between the two
 // (PAB article, Figure 1 caption: measured by the MSE) can be taken on the
 // device.  The dispatcher is stateless: slot parity is the number of
-// recomputes so far, read off the schedule.
+// recomputes so far, read off the schedule.  A type may also be a whole
+// attention module (projections around the attention); its recompute then
+// runs the module and a broadcast step skips all of it.
 #include <stdint.h>
 
 #include "abi.hpp"
@@ -22,8 +24,72 @@ size_t output_elems(const pab_type_desc& t) {
   return (size_t)t.B * t.H * t.F * t.S * t.D;
 }
 
+// The attention module of a type (input projection, attention, output
+// projection), checked as the three calls it makes.
+int check_module(const pab_step_desc* d, const pab_type_desc& t) {
+  if (!t.w_in || !t.w_out || !t.scratch[0] || !t.scratch[1] || !t.scratch[2] || !t.scratch[3])
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: a module needs w_in, w_out and 4 scratch buffers");
+  void* qkv[3] = {t.scratch[0], t.scratch[1], t.scratch[2]};
+  void* slot[3] = {t.slot[0], nullptr, nullptr};
+  int st;
+  if (t.kind == PAB_CROSS) {
+    if (!t.x_text || !t.w_kv)
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: a cross module needs x_text and w_kv");
+    st = check_proj("pab_step_dispatch(proj q)", t.x, t.w_in, qkv, 1, t.B, t.F, t.S, t.H, t.D,
+                    d->dtype, true);
+    if (st) return st;
+    void* kv[3] = {t.scratch[1], t.scratch[2], nullptr};
+    st = check_proj("pab_step_dispatch(proj kv)", t.x_text, t.w_kv, kv, 2, t.B, 1, t.L, t.H, t.D,
+                    d->dtype, true);
+    if (st) return st;
+    st = check_cross_attn(t.scratch[0], t.scratch[1], t.scratch[2], t.scratch[3], t.B, t.H,
+                          (int64_t)t.F * t.S, t.L, t.D, d->dtype, d->softmax_scale, t.text_len);
+  } else {
+    st = check_proj("pab_step_dispatch(proj qkv)", t.x, t.w_in, qkv, 3, t.B, t.F, t.S, t.H, t.D,
+                    d->dtype, true);
+    if (st) return st;
+    st = check_video_attn("pab_step_dispatch(module attention)", t.scratch[0], t.scratch[1],
+                          t.scratch[2], t.scratch[3], t.B, t.H, t.F, t.S, t.D, d->dtype,
+                          d->softmax_scale, t.kind == PAB_TEMPORAL);
+  }
+  if (st) return st;
+  st = check_proj("pab_step_dispatch(proj out)", t.scratch[3], t.w_out, slot, 1, t.B, t.F, t.S,
+                  t.H, t.D, d->dtype, false);
+  return st;
+}
+
 int check_type(const pab_step_desc* d, int a) {
   const pab_type_desc& t = d->types[a];
+  if (t.x) {
+    if (t.kind != PAB_SPATIAL && t.kind != PAB_TEMPORAL && t.kind != PAB_CROSS)
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: unknown attention kind");
+    int st = check_module(d, t);
+    if (st) return st;
+    if (t.slot[1] && !aligned16(t.slot[1]))
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slot[1] must be 16-byte aligned");
+    const size_t bytes = output_elems(t) * dtype_size(d->dtype);
+    if (t.slot[1] && ranges_overlap(t.slot[0], bytes, t.slot[1], bytes))
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slots overlap");
+    // Scratch: q and the attention output are O-sized; a cross module's k, v
+    // hold the text tokens only.
+    const size_t kv_bytes = t.kind == PAB_CROSS
+                                ? (size_t)t.B * t.H * t.L * t.D * dtype_size(d->dtype)
+                                : bytes;
+    const size_t scratch_bytes[4] = {bytes, kv_bytes, kv_bytes, bytes};
+    for (int s = 0; s < 2; ++s)
+      for (int i = 0; t.slot[s] && i < 4; ++i)
+        if (ranges_overlap(t.slot[s], bytes, t.scratch[i], scratch_bytes[i]))
+          return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: a slot overlaps a scratch buffer");
+    if (t.drift && t.slot[1]) {
+      if ((uintptr_t)t.drift & 7u)
+        return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: misaligned drift");
+      if (!d->workspace || !aligned16(d->workspace))
+        return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: drift needs a 16-byte aligned workspace");
+      if (d->workspace_bytes < pab_mse_workspace_bytes((int64_t)output_elems(t)))
+        return fail(PAB_ERR_CAPACITY, "pab_step_dispatch: workspace too small for the drift MSE");
+    }
+    return PAB_OK;
+  }
   const void* probe_out = t.slot[0];
   int st;
   switch (t.kind) {
@@ -97,6 +163,29 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
     if (!desc->recompute[(size_t)step * nt + a]) continue;  // broadcast: no work at all
     mask |= 1u << a;
     int st;
+    if (t.x) {
+      // The whole attention module: projections around the attention.
+      void* qkv[3] = {t.scratch[0], t.scratch[1], t.scratch[2]};
+      if (t.kind == PAB_CROSS) {
+        void* q1[3] = {t.scratch[0], nullptr, nullptr};
+        void* kv[3] = {t.scratch[1], t.scratch[2], nullptr};
+        st = run_proj_in(t.x, t.w_in, q1, 1, t.B, t.F, t.S, t.H, t.D, desc->stream);
+        if (!st) st = run_proj_in(t.x_text, t.w_kv, kv, 2, t.B, 1, t.L, t.H, t.D, desc->stream);
+        if (!st)
+          st = run_cross(t.scratch[0], t.scratch[1], t.scratch[2], t.scratch[3], t.B, t.H,
+                         (int64_t)t.F * t.S, t.L, t.D, desc->dtype, desc->softmax_scale,
+                         t.text_len, desc->stream);
+      } else {
+        st = run_proj_in(t.x, t.w_in, qkv, 3, t.B, t.F, t.S, t.H, t.D, desc->stream);
+        if (!st && t.kind == PAB_SPATIAL)
+          st = run_spatial(qkv[0], qkv[1], qkv[2], t.scratch[3], t.B, t.H, t.F, t.S, t.D,
+                           desc->dtype, desc->softmax_scale, desc->stream);
+        if (!st && t.kind == PAB_TEMPORAL)
+          st = run_temporal(qkv[0], qkv[1], qkv[2], t.scratch[3], t.B, t.H, t.F, t.S, t.D,
+                            desc->dtype, desc->softmax_scale, desc->stream);
+      }
+      if (!st) st = run_proj_out(t.scratch[3], t.w_out, cur, t.B, t.F, t.S, t.H, t.D, desc->stream);
+    } else {
     switch (t.kind) {
       case PAB_SPATIAL:
         st = run_spatial(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
@@ -110,6 +199,7 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
         st = run_cross(t.q, t.k, t.v, cur, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D, desc->dtype,
                        desc->softmax_scale, t.text_len, desc->stream);
         break;
+    }
     }
     if (st) return st;
     if (two && t.drift && count[a] >= 2) {

@@ -18,9 +18,10 @@
 //
 // A 256-thread block computes a 256-token x 192-feature tile (each wave
 // 128 x 96: 12 MFMA accumulators, one wave per SIMD).  k advances in steps
-// of 32 through a 4-stage LDS ring filled by direct global->LDS loads two
-// steps ahead (the output projection's loads gather 16-byte chunks from the
-// head planes).  Blocks are ordered so that the feature tiles of one token
+// of 64 through two LDS stages filled by direct global->LDS loads one step
+// ahead (the output projection's loads gather 16-byte chunks from the head
+// planes); within a step the operands of the next 16-wide k slice are read
+// while the MFMAs of the current one run.  Blocks are ordered so that the feature tiles of one token
 // tile run together on one XCD and share its L2.
 #include "device.hpp"
 #include "launch.hpp"
@@ -33,14 +34,14 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBM = 256;                 // tokens per block
 constexpr int kBN = 192;                 // output features per block
-constexpr int kBK = 32;                  // k per ring stage
-constexpr int kKS = kBK + 8;             // LDS row stride (elements): 5 chunks, odd
+constexpr int kBK = 64;                  // k per ring stage
+constexpr int kKS = kBK + 8;             // LDS row stride (elements): 9 chunks, odd
 constexpr int kKCH = kKS / 8;            // chunks per LDS row (the last is padding)
 constexpr int kRows = kBM + kBN;         // token rows, then weight rows
 constexpr int kStage = kRows * kKS;      // elements
-constexpr int kNst = 4;
-constexpr int kNJ = kRows * kKCH / kWave;          // wave-wide loads per stage (35)
-constexpr int kNJW = (kNJ + kWaves - 1) / kWaves;  // per wave, at most (9)
+constexpr int kNst = 2;
+constexpr int kNJ = kRows * kKCH / kWave;          // wave-wide loads per stage (63)
+constexpr int kNJW = (kNJ + kWaves - 1) / kWaves;  // per wave, at most (16)
 constexpr int kWM = 128, kWN = 96;       // wave tile
 constexpr int kMB = kWM / 32, kNB = kWN / 32;
 constexpr int kOS = kWN + 8;             // epilogue staging row stride (elements)
@@ -48,9 +49,10 @@ static_assert(kRows * kKCH % kWave == 0, "loads cover whole stages");
 static_assert(kBM * kKCH % kWave == 0, "no load straddles token and weight rows");
 static_assert(kNst * kStage * 2 <= 160 * 1024, "LDS ring too large");
 static_assert(kWaves * kWM * kOS <= kNst * kStage, "epilogue staging fits the ring");
-static_assert(2 * kNJW < 64, "vmcnt budget");
+static_assert(kNJW < 64, "vmcnt budget");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // One 16-byte direct global->LDS load per lane: lane l of the wave reads
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs p) {
   const int bm = logical / p.nbn, bn = logical % p.nbn;
   const int m0 = bm * kBM, n0 = bn * kBN;
   const int K = p.K;
-  const int nkt = K / kBK;
+  const int nkt = (K + kBK - 1) / kBK;
 
   // Direct-load plan: load j = wave + 4i covers stage slots 64 j .. 64 j + 63;
   // slot s is chunk s % 5 of stage row s / 5 (rows 0..255 tokens, 256..447
@@ -137,11 +139,20 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs p) {
   auto issue = [&](int kt) {
     const int k0 = kt * kBK;
     const uint32_t st = ring_lds + (uint32_t)((kt % kNst) * kStage * 2);
+    const bool ragged = k0 + kBK > K;  // the last step of a K that is not a multiple of 64
 #pragma unroll
     for (int i = 0; i < kNJW; ++i) {
       const int j = wave + kWaves * i;
       if (i + 1 < kNJW || j < kNJ) {
         const uint32_t lds = st + (uint32_t)(j * 1024);
+        if (ragged) {
+          // Chunks past K hold zeros (written here, never loaded over).
+          const int ch = (j * kWave + lane) % kKCH;
+          if (ch < kKCH - 1 && k0 + ch * 8 >= K) {
+            *LDS_PTR(u32x4, lds + (uint32_t)(lane * 16)) = u32x4{0u, 0u, 0u, 0u};
+            continue;
+          }
+        }
         if (j * kWave < kBM * kKCH) {  // token rows (wave-uniform)
           uint32_t off;
           if (GATHER) {
@@ -158,17 +169,13 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs p) {
       }
     }
   };
-  const int nj_wave = (kNJ - wave + kWaves - 1) / kWaves;
-  // Before stage kt is read: its loads have landed (those of kt+1 may still
-  // be in flight), and every wave's loads are visible.
+  // Before stage kt is read: its loads have landed and every wave's loads
+  // are visible; the other stage (read last in step kt-1) is then refilled
+  // with step kt+1, which lands while step kt computes.
   auto sync_stage = [&](int kt) {
-    if (kt + 1 < nkt) {
-      if (nj_wave == kNJW) wait_vmcnt<kNJW>(); else wait_vmcnt<kNJW - 1>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 2 < nkt) issue(kt + 2);
+    if (kt + 1 < nkt) issue(kt + 1);
   };
 
   // Wave tile: tokens wm*128.., features wn*96.. of the block tile.
@@ -183,23 +190,29 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs p) {
     for (int mb = 0; mb < kMB; ++mb) acc[nb][mb] = zero16();
 
   issue(0);
-  if (nkt > 1) issue(1);
   for (int kt = 0; kt < nkt; ++kt) {
     sync_stage(kt);
     const uint32_t st = ring_lds + (uint32_t)((kt % kNst) * kStage * 2);
-#pragma unroll
-    for (int k16 = 0; k16 < kBK / 16; ++k16) {
-      bf16x8 wop[kNB], xop[kMB];
+    // Operands of the next 16-wide k step are read while the MFMAs of the
+    // current one run.
+    bf16x8 wop[2][kNB], xop[2][kMB];
+    auto load_ops = [&](int k16, bf16x8 (&wo)[kNB], bf16x8 (&xo)[kMB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
-        wop[nb] = *LDS_PTR(const bf16x8, st + wlane + (uint32_t)((nb * 32 * kKS + k16 * 16) * 2));
+        wo[nb] = *LDS_PTR(const bf16x8, st + wlane + (uint32_t)((nb * 32 * kKS + k16 * 16) * 2));
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
-        xop[mb] = *LDS_PTR(const bf16x8, st + xlane + (uint32_t)((mb * 32 * kKS + k16 * 16) * 2));
+        xo[mb] = *LDS_PTR(const bf16x8, st + xlane + (uint32_t)((mb * 32 * kKS + k16 * 16) * 2));
+    };
+    load_ops(0, wop[0], xop[0]);
+#pragma unroll
+    for (int k16 = 0; k16 < kBK / 16; ++k16) {
+      if (k16 + 1 < kBK / 16) load_ops(k16 + 1, wop[(k16 + 1) & 1], xop[(k16 + 1) & 1]);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[nb][mb] = mfma32(wop[nb], xop[mb], acc[nb][mb]);
+        for (int mb = 0; mb < kMB; ++mb)
+          acc[nb][mb] = mfma32(wop[k16 & 1][nb], xop[k16 & 1][mb], acc[nb][mb]);
     }
   }
 
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs p) {
 hipError_t launch_proj_bf16(const void* x, const void* w, void* const out[3], int64_t M, int N,
                             int K, int T, int H, int D, bool gather, bool scatter,
                             hipStream_t stream) {
-  if (K % kBK != 0 || M < 1 || N < 1) return hipErrorInvalidValue;
+  if (K % 32 != 0 || M < 1 || N < 1) return hipErrorInvalidValue;
   ProjArgs p;
   p.x = (const bf16*)x;
   p.w = (const bf16*)w;

@@ -46,6 +46,13 @@ class Config:
     # encoder's would) instead of following the perturbation model.
     text_len: tuple | None = None
     const_text: bool = False
+    # Whole attention modules: each recompute runs the input projection, the
+    # attention and the output projection; a broadcast step skips all three.
+    module: bool = False
+
+    @property
+    def C(self):
+        return self.H * self.D
 
     @property
     def video_shape(self):
@@ -84,6 +91,15 @@ CONFIGS = {
                      "480p-latent block, CFG batch 2 with padded prompts (77 and 1 real text "
                      "tokens of 120, constant text K/V), 30 steps",
                      text_len=(77, 1), const_text=True),
+    # Attention modules (projections around each attention).
+    "mod_small": Config("mod_small", "bf16", 1, 4, 4, 100, 64, 16, 10,
+                        ("spatial", "temporal", "cross"), (2, 3, 5), 1, 7,
+                        "attention modules: 4 frames x 100 tokens, 4 heads x 64 (C = 256), "
+                        "16 text tokens, 10 steps", module=True),
+    "b480m": Config("b480m", "bf16", 1, 16, 48, 1590, 72, 120, 30,
+                    ("spatial", "temporal", "cross"), (2, 4, 6), 1, 8,
+                    "480p-latent block as attention modules (C = 1152 projections around each "
+                    "attention), 30 steps", module=True),
 }
 
 TYPE_INDEX = {"spatial": 0, "temporal": 1, "cross": 2}
@@ -112,6 +128,15 @@ def attn_bytes(cfg: Config, kind: str) -> int:
     return 4 * n
 
 
+def proj_flops(cfg: Config, kind: str) -> int:
+    """Multiply-adds (2 flops each) of a module's input and output
+    projections: token rows x C x C per projected tensor."""
+    C_, tokens = cfg.C, cfg.B * cfg.F * cfg.S
+    if kind == "cross":
+        return 2 * C_ * C_ * (2 * tokens + 2 * cfg.B * cfg.L)
+    return 2 * C_ * C_ * 4 * tokens
+
+
 def mse_bytes(cfg: Config) -> int:
     return 2 * cfg.B * cfg.H * cfg.F * cfg.S * cfg.D * cfg.elem_bytes
 
@@ -119,7 +144,9 @@ def mse_bytes(cfg: Config) -> int:
 # ------------------------------------------------------------------- inputs
 
 class Inputs:
-    """Per (block, type, step) Q/K/V device tensors.
+    """Per (block, type, step) Q/K/V device tensors (module configurations:
+    the module input x, plus the text tokens for a cross attention, and fixed
+    projection weights per (block, type)).
 
     resident=True generates every needed step up front (the timed region then
     only reads HBM); otherwise tensors are generated on demand, outside the
@@ -133,25 +160,45 @@ class Inputs:
         self.tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.store = {}
         self.scratch = {}
+        self._w = {}
         if resident:
             for (b, a, i) in steps_needed:
                 self.store[(b, a, i)] = self._make(b, a, i, None)
 
     def _shapes(self, a):
-        kind = self.cfg.kinds[a]
-        kv = self.cfg.text_shape if kind == "cross" else self.cfg.video_shape
-        return self.cfg.video_shape, kv
+        cfg = self.cfg
+        kind = cfg.kinds[a]
+        if cfg.module:
+            x = (cfg.B, cfg.F * cfg.S, cfg.C)
+            return (x, (cfg.B, cfg.L, cfg.C)) if kind == "cross" else (x,)
+        kv = cfg.text_shape if kind == "cross" else cfg.video_shape
+        return cfg.video_shape, kv, kv
+
+    def weights(self, b, a):
+        """(w_in, w_kv or None, w_out) of a module configuration."""
+        if (b, a) not in self._w:
+            cfg = self.cfg
+            t = TYPE_INDEX[cfg.kinds[a]]
+            cross = cfg.kinds[a] == "cross"
+            mk = lambda shape, which: synth.gpu_weight(shape, cfg.seed, b, t, which, cfg.dtype,
+                                                       self.device)
+            self._w[(b, a)] = (mk(((1 if cross else 3) * cfg.C, cfg.C), 0),
+                               mk((2 * cfg.C, cfg.C), 1) if cross else None,
+                               mk((cfg.C, cfg.C), 2))
+        return self._w[(b, a)]
 
     def _make(self, b, a, i, out):
-        qs, kvs = self._shapes(a)
+        shapes = self._shapes(a)
         t = TYPE_INDEX[self.cfg.kinds[a]]
         res = []
         const = self.cfg.const_text and self.cfg.kinds[a] == "cross"
-        for tensor, shape in ((0, qs), (1, kvs), (2, kvs)):
+        # Module inputs use their own generator streams (tensors 3 and 4).
+        first = 3 if self.cfg.module else 0
+        for tensor, shape in enumerate(shapes, start=first):
             dst = None if out is None else out[tensor]
             res.append(synth.gpu_tensor(shape, self.cfg.seed, b, t, tensor, i, self.cfg.N,
                                         self.cfg.dtype, self.device, out=dst,
-                                        perturb=not (const and tensor > 0)))
+                                        perturb=not (const and tensor != first)))
         return tuple(res)
 
     def get(self, b, a, i):
@@ -160,9 +207,8 @@ class Inputs:
         import torch
 
         if a not in self.scratch:
-            qs, kvs = self._shapes(a)
             self.scratch[a] = tuple(torch.empty(s, dtype=self.tdt, device=self.device)
-                                    for s in (qs, kvs, kvs))
+                                    for s in self._shapes(a))
         return self._make(b, a, i, self.scratch[a])
 
 
@@ -183,9 +229,14 @@ class Trajectory:
         self.T = len(cfg.kinds)
         tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         # Cache: two O-sized slots per (block, type), resident in HBM.
-        self.slots = [[(torch.empty(cfg.video_shape, dtype=tdt, device=self.device),
-                        torch.empty(cfg.video_shape, dtype=tdt, device=self.device))
+        out_shape = (cfg.B, cfg.F * cfg.S, cfg.C) if cfg.module else cfg.video_shape
+        self.slots = [[(torch.empty(out_shape, dtype=tdt, device=self.device),
+                        torch.empty(out_shape, dtype=tdt, device=self.device))
                        for _ in range(self.T)] for _ in range(cfg.blocks)]
+        # Module intermediates (q, k, v, attention output), shared by every
+        # (block, type): the dispatches run one after another on one stream.
+        self.mod_scratch = ([torch.empty(cfg.video_shape, dtype=tdt, device=self.device)
+                             for _ in range(4)] if cfg.module else None)
         n = int(np.prod(cfg.video_shape))
         self.ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=self.device)
         self.drift_out = torch.zeros((cfg.blocks, self.T, cfg.N), dtype=torch.float64,
@@ -210,6 +261,9 @@ class Trajectory:
                 t[0].drift = None
                 if cfg.kinds[a] == "cross" and cfg.text_len is not None:
                     t[0].text_len = self._text_len.ctypes.data_as(C.POINTER(C.c_int32))
+                if cfg.module:
+                    for j in range(4):
+                        t[0].scratch[j] = self.mod_scratch[j].data_ptr()
                 d = lib.StepDesc(
                     num_steps=cfg.N, num_types=1,
                     recompute=self._rec_cols[a].ctypes.data_as(C.POINTER(C.c_uint8)),
@@ -244,7 +298,14 @@ class Trajectory:
                         d = self._descs[b][a]
                         t = self._types[b * self.T + a]
                         rec = bool(self.recompute[i, a])
-                        if rec:
+                        if rec and cfg.module:
+                            x = self.inputs.get(b, a, i)
+                            w_in, w_kv, w_out = self.inputs.weights(b, a)
+                            t[0].x = x[0].data_ptr()
+                            t[0].x_text = x[1].data_ptr() if len(x) > 1 else None
+                            t[0].w_in, t[0].w_out = w_in.data_ptr(), w_out.data_ptr()
+                            t[0].w_kv = w_kv.data_ptr() if w_kv is not None else None
+                        elif rec:
                             q, k, v = self.inputs.get(b, a, i)
                             t[0].q, t[0].k, t[0].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
                         if events and rec:
@@ -271,7 +332,7 @@ class Trajectory:
         return {"masks": masks, "outs": outs, "brackets": brackets}
 
     def _mse(self, a_ptr, b_ptr, out):
-        n = int(np.prod(self.cfg.video_shape))
+        n = int(np.prod(self.cfg.video_shape))  # a module output has as many elements
         st = lib.load().pab_attn_diff_mse(
             C.c_void_p(a_ptr), C.c_void_p(b_ptr), n,
             lib.PAB_BF16 if self.cfg.dtype == "bf16" else lib.PAB_F32,
@@ -287,8 +348,11 @@ class Trajectory:
         raise KeyError(ptr)
 
     def flops(self) -> int:
-        """Algorithmic attention flops this trajectory executes."""
-        return sum(int(self.counts[a]) * attn_flops(self.cfg, k) * self.cfg.blocks
+        """Algorithmic flops this trajectory executes (attention, plus the
+        projections of a module configuration)."""
+        per = lambda k: attn_flops(self.cfg, k) + (proj_flops(self.cfg, k) if self.cfg.module
+                                                    else 0)
+        return sum(int(self.counts[a]) * per(k) * self.cfg.blocks
                    for a, k in enumerate(self.cfg.kinds))
 
 

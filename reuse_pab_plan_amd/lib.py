@@ -69,6 +69,12 @@ class TypeDesc(C.Structure):
         ("L", C.c_int32),
         ("drift", C.c_void_p),
         ("text_len", C.POINTER(C.c_int32)),
+        ("x", C.c_void_p),
+        ("x_text", C.c_void_p),
+        ("w_in", C.c_void_p),
+        ("w_kv", C.c_void_p),
+        ("w_out", C.c_void_p),
+        ("scratch", C.c_void_p * 4),
     ]
 
 

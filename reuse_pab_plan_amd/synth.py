@@ -15,6 +15,12 @@ between, which gives consecutive-step differences the U shape the PAB article
 reports ("Implementation", first observation).  Values are drawn in fp32 and
 rounded to the working dtype (bf16 rounds to nearest even).
 
+Attention-module workloads draw the module input instead: token-major
+``x`` [B, F*S, C] (and the text tokens [B, L, C] of a cross attention)
+follow the same perturbation model, and each projection weight is a fixed
+``N(0, 1/C)`` matrix per (block, type), so that projected Q/K/V have unit
+variance like the attention-only inputs.
+
 Two generators draw the same distribution:
 
 * ``cpu_tensor`` -- numpy PCG64 streams, for small shapes and CPU tests;
@@ -87,3 +93,19 @@ def gpu_tensor(shape, config_seed, block, type_idx, tensor, step, n_steps, dtype
         return x.to(tdt)
     out.copy_(x)
     return out
+
+
+WEIGHTS = {"w_in": 0, "w_kv": 1, "w_out": 2}
+
+
+def gpu_weight(shape, config_seed, block, type_idx, which, dtype="bf16", device="cuda"):
+    """A fixed projection weight [out, in] ~ N(0, 1/in), drawn on the device
+    (the same at every step); ``which`` indexes ``WEIGHTS``."""
+    import torch
+
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+    g.manual_seed(stream_id(config_seed, block, type_idx, 8 + which, -1))
+    w = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    w.mul_(float(shape[1]) ** -0.5)
+    return w.to(tdt)

@@ -153,3 +153,47 @@ def test_dispatch_validation_codes():
     d.workspace, d.workspace_bytes = 0x7c000000, 8
     assert L.pab_step_dispatch(C.byref(d), 0, None, None) == lib.PAB_ERR_CAPACITY
     assert L.pab_step_dispatch(None, 0, None, None) == lib.PAB_ERR_INVALID_ARG
+
+
+def test_dispatch_module_rejects_missing_weights_and_fp32():
+    # A module (x set) needs w_in, w_out and four scratch buffers, and is
+    # built for bf16 only; every check runs on the host before any launch.
+    sched = np.ones((2, 1), dtype=np.uint8)
+    for dtype, missing, code in ((lib.PAB_BF16, "w_out", lib.PAB_ERR_INVALID_ARG),
+                                 (lib.PAB_F32, None, lib.PAB_ERR_UNSUPPORTED)):
+        t = (lib.TypeDesc * 1)()
+        t[0].kind = lib.KINDS["spatial"]
+        t[0].slot[0], t[0].slot[1] = 0x100000, 0x200000
+        t[0].B, t[0].H, t[0].F, t[0].S, t[0].D = 1, 2, 2, 8, 64
+        t[0].x, t[0].w_in, t[0].w_out = 0x300000, 0x400000, 0x500000
+        for j in range(4):
+            t[0].scratch[j] = 0x600000 + j * 0x100000
+        if missing:
+            setattr(t[0], missing, None)
+        d = lib.StepDesc(num_steps=2, num_types=1,
+                         recompute=sched.ctypes.data_as(C.POINTER(C.c_uint8)),
+                         types=C.cast(t, C.POINTER(lib.TypeDesc)), dtype=dtype,
+                         softmax_scale=0.0, workspace=None, workspace_bytes=0, stream=None)
+        mask = C.c_uint32(0)
+        ptrs = (C.c_void_p * 1)()
+        st = lib.load().pab_step_dispatch(C.byref(d), 0, C.byref(mask), ptrs)
+        assert st == code, (dtype, missing, st)
+
+
+def test_dispatch_module_rejects_slot_scratch_overlap():
+    sched = np.ones((2, 1), dtype=np.uint8)
+    t = (lib.TypeDesc * 1)()
+    t[0].kind = lib.KINDS["temporal"]
+    t[0].B, t[0].H, t[0].F, t[0].S, t[0].D = 1, 2, 2, 8, 64
+    t[0].slot[0], t[0].slot[1] = 0x100000, 0x200000
+    t[0].x, t[0].w_in, t[0].w_out = 0x300000, 0x400000, 0x500000
+    for j in range(4):
+        t[0].scratch[j] = 0x600000 + j * 0x100000
+    t[0].scratch[3] = 0x200000 + 64   # inside slot[1]
+    d = lib.StepDesc(num_steps=2, num_types=1,
+                     recompute=sched.ctypes.data_as(C.POINTER(C.c_uint8)),
+                     types=C.cast(t, C.POINTER(lib.TypeDesc)), dtype=lib.PAB_BF16,
+                     softmax_scale=0.0, workspace=None, workspace_bytes=0, stream=None)
+    mask = C.c_uint32(0)
+    ptrs = (C.c_void_p * 1)()
+    assert lib.load().pab_step_dispatch(C.byref(d), 0, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG

@@ -1,0 +1,159 @@
+"""GPU tests of attention modules through the step dispatcher (C ABI).
+
+PAB article, "Implementation": a broadcast step reuses the attention
+module's output, so the input projection, the attention and the output
+projection are all skipped; a recompute runs all three.  Over a trajectory:
+the dispatch mask equals the oracle's schedule, a broadcast step hands back
+the source step's slot with identical bytes, and every recomputed output
+matches the fp64 oracle module (whole tensors on the small workload, sampled
+tokens at the 480p-latent shape).
+
+Tolerance, from the arithmetic: the path rounds to bf16 four times in a row
+(the projected q/k/v, the softmax probabilities, the attention output and the
+module output), each within 2^-9 relative; emulating exactly those roundings
+around the fp64 oracle on the CPU gives a relative L2 error near 4e-3 and a
+largest error near 5e-3 of max|ref| on these workloads.  The bound is about
+twice that: max error <= 2^-6 * max|ref| and relative L2 <= 2^-7.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reuse_pab_plan_amd import harness, lib
+
+pytestmark = pytest.mark.gpu
+TOL_MAX, TOL_L2 = 2.0 ** -6, 2.0 ** -7
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.load()
+
+
+def _host(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def _fingerprint(t):
+    x = t.view(torch.int16).to(torch.int64).flatten()
+    idx = torch.arange(x.numel(), device=x.device, dtype=torch.int64)
+    return (int(x.sum()), int((x * (idx % 65521 + 1)).sum()))
+
+
+def _compare(got, ref, label):
+    err = got - ref
+    mx = float(np.abs(err).max()) / float(np.abs(ref).max())
+    rl = float(np.linalg.norm(err) / np.linalg.norm(ref))
+    print(f"[parity] {label}: max_abs/max|ref|={mx:.2e} rel_l2={rl:.2e}", flush=True)
+    assert mx <= TOL_MAX and rl <= TOL_L2, (label, mx, rl)
+
+
+def _module_full(cfg, kind, x, w):
+    w_in, w_kv, w_out = (None if t is None else _host(t) for t in w)
+    return oracle.module(kind, _host(x[0]), w_in, w_out, cfg.H, cfg.D, cfg.F, cfg.S,
+                         x_text=_host(x[1]) if len(x) > 1 else None, w_kv=w_kv,
+                         text_len=list(cfg.text_len) if cfg.text_len else None)
+
+
+def _module_sampled(cfg, kind, x, w, slot, label):
+    """Module outputs at sampled tokens of entry 0, from the oracle's own
+    functions on the tokens each output depends on."""
+    H, F, S, D, C = cfg.H, cfg.F, cfg.S, cfg.D, cfg.C
+    w_in, w_kv, w_out = (None if t is None else _host(t) for t in w)
+    xs = x[0][0]                                           # [F*S, C], device
+    y = slot[0]
+    if kind == "spatial":
+        f = F - 1
+        rows = np.arange(0, S, max(1, S // 100))
+        q, k, v = oracle.proj_in(_host(xs[f * S:(f + 1) * S])[None], w_in, H, D, 1, S)
+        o = np.stack([oracle.spatial_rows(q, k, v, 0, h, 0, rows) for h in range(H)])
+        ref = oracle.proj_out(o[None, :, None], w_out)[0]
+        got = _host(y[f * S + rows])
+    elif kind == "temporal":
+        pos = np.arange(0, S, max(1, S // 24))
+        idx = (np.arange(F)[:, None] * S + pos[None, :]).reshape(-1)
+        q, k, v = oracle.proj_in(_host(xs[idx])[None], w_in, H, D, F, len(pos))
+        ref = oracle.proj_out(oracle.temporal(q, k, v), w_out)[0]
+        got = _host(y[idx])
+    else:
+        rows = np.arange(0, F * S, max(1, F * S // 400))
+        (q,) = oracle.proj_in(_host(xs[rows])[None], w_in, H, D, 1, len(rows))
+        k, v = oracle.proj_in(_host(x[1][0])[None], w_kv, H, D, 1, cfg.L)
+        n_text = [cfg.text_len[0]] if cfg.text_len else None
+        ref = oracle.proj_out(oracle.cross(q, k[:, :, 0], v[:, :, 0], text_len=n_text), w_out)[0]
+        got = _host(y[rows])
+    _compare(got, ref, label)
+
+
+def _run(cfg, check, check_steps=None):
+    dev = torch.device("cuda:0")
+    traj = harness.Trajectory(cfg, pab=True, device=dev)
+    traj.inputs = harness.Inputs(cfg, traj.steps_needed(), device=dev)
+    rec, src, cnt = oracle.schedule(cfg.N, list(cfg.ranges))
+    assert np.array_equal(traj.recompute, rec) and np.array_equal(traj.counts, cnt)
+    prints, checked = {}, []
+
+    def on_step(i, outs):
+        torch.cuda.synchronize()
+        for a, kind in enumerate(cfg.kinds):
+            ptr = outs[0][i][a]
+            slot = traj.slot_tensor(0, a, ptr)
+            j = int(src[i, a])
+            if j == i:
+                prints[(a, i)] = _fingerprint(slot)
+                if check_steps is None or i in check_steps:
+                    x = traj.inputs.get(0, a, i)
+                    check(cfg, kind, x, traj.inputs.weights(0, a), slot,
+                          f"{cfg.name} {kind} step {i}")
+                    checked.append((a, i))
+            else:
+                assert ptr == outs[0][j][a], "reuse must hand back the source slot"
+                assert _fingerprint(slot) == prints[(a, j)], "reused bytes changed"
+
+    res = traj.run(on_step=on_step)
+    for i in range(cfg.N):
+        for a in range(len(cfg.kinds)):
+            assert ((int(res["masks"][0, i]) >> a) & 1) == rec[i, a]
+    assert checked
+    return traj
+
+
+def test_module_trajectory_small_every_recompute():
+    _need_gpu()
+    cfg = harness.CONFIGS["mod_small"]
+
+    def check(cfg, kind, x, w, slot, label):
+        _compare(_host(slot), _module_full(cfg, kind, x, w), label)
+
+    traj = _run(cfg, check)
+    # The oracle's trajectory over the same inputs: the same schedule, and
+    # module outputs that the GPU slots match at the last step.
+    def inputs_fn(i, a):
+        return {"x": traj.inputs.get(0, a, i), "w": traj.inputs.weights(0, a)}
+
+    ref = oracle.trajectory(cfg.N, list(cfg.kinds), list(cfg.ranges), inputs_fn,
+                            compute=lambda kind, d: _module_full(cfg, kind, d["x"], d["w"]))
+    assert ref["calls"] == int(traj.counts.sum())
+
+
+def test_module_trajectory_b480_sampled():
+    _need_gpu()
+    cfg = harness.CONFIGS["b480m"]
+    w0 = -(-15 * cfg.N // 100)
+    _run(cfg, _module_sampled, check_steps=(0, w0, cfg.N - 1))
+
+
+def test_module_padded_prompts():
+    _need_gpu()
+    import dataclasses
+
+    cfg = dataclasses.replace(harness.CONFIGS["mod_small"], name="mod_cfg", B=2,
+                              text_len=(11, 1), const_text=True)
+
+    def check(cfg, kind, x, w, slot, label):
+        _compare(_host(slot), _module_full(cfg, kind, x, w), label)
+
+    _run(cfg, check)

@@ -125,3 +125,23 @@ def test_synth_streams_distinct_and_deterministic():
 def test_attn_used_by_trajectory_is_the_definition():
     x = make_inputs(3)(0, 0)
     assert np.array_equal(direct("spatial", x), attn_fp64(x["q"], x["k"], x["v"]))
+
+
+def test_trajectory_custom_compute_is_called_at_recomputes_only():
+    # A compute function replaces the attention (an attention module, say):
+    # it runs exactly at recompute steps, and every output is the one of the
+    # step's source.
+    seen = []
+
+    def compute(kind, x):
+        seen.append((x["step"], kind))
+        return np.array([x["step"]])
+
+    res = trajectory(12, ["spatial", "cross"], [2, 4],
+                            lambda i, a: {"step": i}, compute=compute)
+    rec, src = res["recompute"], res["source"]
+    assert sorted(seen) == sorted((i, k) for i in range(12) for a, k in enumerate(["spatial", "cross"])
+                                  if rec[i, a])
+    for i in range(12):
+        for a in range(2):
+            assert int(res["outputs"][i][a][0]) == int(src[i, a])

@@ -76,3 +76,24 @@ def test_head_relabelling():
     (qp,) = oracle.proj_in(x, wp, H, D, F, S)
     for h, p in enumerate(perm):
         assert np.array_equal(qp[0, h], q[0, p])
+
+
+def test_module_identity_projections_is_attention():
+    # With identity projections the module is the attention itself (its
+    # output read token-major).
+    B, F, S, H, D = 1, 2, 5, 2, 8
+    C = H * D
+    x = rng.standard_normal((B, F * S, C))
+    eye3 = np.concatenate([np.eye(C)] * 3)
+    for kind, fn in (("spatial", oracle.spatial), ("temporal", oracle.temporal)):
+        got = oracle.module(kind, x, eye3, np.eye(C), H, D, F, S)
+        (q,) = oracle.proj_in(x, np.eye(C), H, D, F, S)
+        want = oracle.proj_out(fn(q, q, q), np.eye(C))
+        assert np.max(np.abs(got - want)) <= 1e-12
+    xt = rng.standard_normal((B, 3, C))
+    got = oracle.module("cross", x, np.eye(C), np.eye(C), H, D, F, S, x_text=xt,
+                        w_kv=np.concatenate([np.eye(C)] * 2), text_len=[2])
+    (q,) = oracle.proj_in(x, np.eye(C), H, D, F, S)
+    (kt,) = oracle.proj_in(xt, np.eye(C), H, D, 1, 3)
+    want = oracle.proj_out(oracle.cross(q, kt[:, :, 0], kt[:, :, 0], text_len=[2]), np.eye(C))
+    assert np.max(np.abs(got - want)) <= 1e-12
