@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--off-steps", type=int, default=5, help="timed PAB-off trajectories")
     ap.add_argument("--config", default="b480")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--module-config", default="b480m",
+                    help="attention-module workload timed after the main line ('' to skip)")
+    ap.add_argument("--module-steps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
@@ -155,6 +158,81 @@ def cpu_baseline(cfg, traj_on, inputs, budget_s):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def module_leg(name, steps, dev, stream):
+    """Attention modules (input projection, attention, output projection
+    around each attention type) over a PAB-on and a PAB-off trajectory, and
+    the two projection GEMMs timed alone at the workload's shapes."""
+    import numpy as np
+    import torch
+
+    from reuse_pab_plan_amd import harness, lib
+
+    cfg = harness.CONFIGS[name]
+    on = harness.Trajectory(cfg, pab=True, device=dev, stream=stream, drift=False)
+    off = harness.Trajectory(cfg, pab=False, device=dev, stream=stream, drift=False)
+    inputs = harness.Inputs(cfg, off.steps_needed(), device=dev, resident=True)
+    on.inputs = off.inputs = inputs
+    on.run(events=False)
+    off.run(events=False)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for label, traj, n in (("on", on, steps), ("off", off, 1)):
+        per = [[] for _ in cfg.kinds]
+        start.record(stream)
+        for _ in range(n):
+            r = traj.run(events=True)
+            for a in range(len(cfg.kinds)):
+                per[a] += r["brackets"]["attn"][a]
+        stop.record(stream)
+        torch.cuda.synchronize()
+        res[label] = (start.elapsed_time(stop) / n, per)
+    on_ms, per_on = res["on"]
+    off_ms, _ = res["off"]
+    out = {"workload": cfg.desc, "name": cfg.name,
+           "pab_on_ms_per_trajectory": on_ms, "pab_off_ms_per_trajectory": off_ms,
+           "pab_speedup": off_ms / on_ms,
+           "tflops_pab_on": on.flops() / (on_ms * 1e-3) / 1e12,
+           "module_ms": {k: stats_ms(per_on[a])["mean_ms"] for a, k in enumerate(cfg.kinds)}}
+    # The GEMMs alone, on the stream they are launched on, rotating over
+    # three input sets so the timed launches read HBM.
+    B, H, F, S, D = cfg.video_shape
+    C_, T = cfg.C, F * S
+    xs = [inputs.get(0, 0, i)[0] for i in range(3)]
+    w_in, _, w_out = inputs.weights(0, 0)
+    bufs = [[torch.empty(cfg.video_shape, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            for _ in range(3)]
+    ys = [torch.empty((B, T, C_), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    st = stream.cuda_stream
+    gemms = {
+        "proj_in": (lambda i: lib.pab_proj_in(xs[i % 3], w_in, bufs[i % 3], F, S, H, D, stream=st),
+                    2 * B * T * 3 * C_ * C_),
+        "proj_out": (lambda i: lib.pab_proj_out(bufs[i % 3][0], w_out, ys[i % 3], stream=st),
+                     2 * B * T * C_ * C_),
+    }
+    out["gemm"] = {}
+    for g, (fn, flops) in gemms.items():
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = []
+        for i in range(12):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(i)
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        sm = stats_ms(ev)
+        sm["flops_per_launch"] = flops
+        sm["tflops"] = flops / (sm["mean_ms"] * 1e-3) / 1e12
+        sm["frac_mfma"] = sm["tflops"] / PEAK_BF16_TFLOPS
+        out["gemm"][g] = sm
+    del on, off, inputs, bufs, ys
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -328,6 +406,13 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if args.module_config:
+        out["module"] = module_leg(args.module_config, args.module_steps, dev, stream)
+        m = out["module"]
+        log(f"modules {m['name']}: PAB on {m['pab_on_ms_per_trajectory']:.2f} ms, off "
+            f"{m['pab_off_ms_per_trajectory']:.2f} ms; proj_in "
+            f"{m['gemm']['proj_in']['tflops']:.0f} TFLOP/s, proj_out "
+            f"{m['gemm']['proj_out']['tflops']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, traj_on, inputs, args.cpu_budget)
