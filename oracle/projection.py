@@ -8,7 +8,7 @@ the output projection (the features the article calls x_t pass through
 them).  Skipping the attention on a broadcast step therefore skips both
 projections with it: the cached quantity is the attention module's output.
 
-Readings where the pages are open (repeated in the design doc):
+Readings where the pages are open:
 
 19. Weights use the layout of a linear layer, ``w[out_features, in_features]``
     with ``y = x @ w.T``, no bias.  Hidden size C = H * D; the input

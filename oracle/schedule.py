@@ -13,7 +13,7 @@ What the pages fix (restated, not quoted):
   change, the wider its range (spatial changes most, cross attention least).
   PAB abstract: the ranges form a "pyramid" set per type by its variance.
 
-Readings taken where the pages are open (each is repeated in the design doc):
+Readings taken where the pages are open:
 
 1. ``r`` (the range) is the number of following steps that reuse one computed
    output; the recompute period inside the window is ``r + 1``.  ``r = 0`` is
@@ -129,7 +129,7 @@ def calibrate_ranges(diff, candidates, lo_pct: int = 15, hi_pct: int = 85):
     outputs of consecutive steps (Figure 1 caption).  The PAB abstract calls
     the resulting set of ranges a pyramid chosen by each type's variance.
 
-    Readings where the pages are open (repeated in the design doc):
+    Readings where the pages are open:
 
     5. The change of type a is scored by the plain mean of diff[i][a] over the
        steps i whose output and predecessor's output both lie in the stable
