@@ -129,14 +129,20 @@ def test_module_trajectory_small_every_recompute():
         _compare(_host(slot), _module_full(cfg, kind, x, w), label)
 
     traj = _run(cfg, check)
-    # The oracle's trajectory over the same inputs: the same schedule, and
-    # module outputs that the GPU slots match at the last step.
+    # The oracle's own trajectory over the same inputs: as many module
+    # evaluations as the GPU schedule recomputes, and the outputs it hands
+    # out at the last step match the slots the GPU hands out there.
     def inputs_fn(i, a):
         return {"x": traj.inputs.get(0, a, i), "w": traj.inputs.weights(0, a)}
 
     ref = oracle.trajectory(cfg.N, list(cfg.kinds), list(cfg.ranges), inputs_fn,
                             compute=lambda kind, d: _module_full(cfg, kind, d["x"], d["w"]))
     assert ref["calls"] == int(traj.counts.sum())
+    last = traj.run(max_steps=cfg.N)["outs"][0][cfg.N - 1]
+    torch.cuda.synchronize()
+    for a, kind in enumerate(cfg.kinds):
+        _compare(_host(traj.slot_tensor(0, a, last[a])), ref["outputs"][cfg.N - 1][a],
+                 f"{cfg.name} {kind} oracle trajectory, last step")
 
 
 def test_module_trajectory_b480_sampled():
@@ -152,6 +158,32 @@ def test_module_padded_prompts():
 
     cfg = dataclasses.replace(harness.CONFIGS["mod_small"], name="mod_cfg", B=2,
                               text_len=(11, 1), const_text=True)
+
+    def check(cfg, kind, x, w, slot, label):
+        _compare(_host(slot), _module_full(cfg, kind, x, w), label)
+
+    _run(cfg, check)
+
+
+MODULE_SHAPES = [
+    # name, changes to the small workload
+    ("full3d_like", dict(kinds=("spatial", "cross"), ranges=(2, 4), B=2, H=6, F=1, S=300, D=64,
+                         L=20, N=8)),
+    ("d128", dict(H=2, F=3, S=70, D=128, L=9, N=6, ranges=(1, 2, 3))),
+    ("c288_long_text", dict(H=4, F=2, S=130, D=72, L=120, N=5, ranges=(1, 1, 1))),
+    ("d32_one_token_off", dict(H=8, F=5, S=33, D=32, L=1, N=4, ranges=(0, 0, 0))),
+]
+
+
+@pytest.mark.parametrize("name,changes", MODULE_SHAPES, ids=[m[0] for m in MODULE_SHAPES])
+def test_module_shapes(name, changes):
+    # Head widths 32..128, hidden sizes that are multiples of 32 but not of
+    # 64 or of the 384-wide feature tile, ragged token tiles, one frame, one
+    # text token, PAB off.
+    _need_gpu()
+    import dataclasses
+
+    cfg = dataclasses.replace(harness.CONFIGS["mod_small"], name=name, **changes)
 
     def check(cfg, kind, x, w, slot, label):
         _compare(_host(slot), _module_full(cfg, kind, x, w), label)
