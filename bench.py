@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--module-config", default="b480m",
                     help="attention-module workload timed after the main line ('' to skip)")
     ap.add_argument("--module-steps", type=int, default=3)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the sustained-peak microbenchmarks (measured roofline denominators)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
@@ -338,6 +340,11 @@ def main():
         }
         log(f"calibrated ranges {calibration['ranges']} (configured {dict(zip(cfg.kinds, cfg.ranges))})")
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = lib.measure_peaks(dev, stream)
+        log("measured peaks: " + ", ".join(f"{k} {v:.0f}" for k, v in peaks.items()))
+
     kernels = {}
     for a, kind in enumerate(cfg.kinds):
         st = stats_ms(brackets["attn"][a])
@@ -352,8 +359,12 @@ def main():
         })
         if kind == "spatial":
             st["frac_mfma"] = st["tflops"] / PEAK_BF16_TFLOPS
+            if peaks:
+                st["frac_mfma_measured_peak"] = st["tflops"] / peaks["mfma_bf16_tflops"]
         else:
             st["frac_hbm"] = st["gbs"] / PEAK_HBM_GBS
+            if peaks:
+                st["frac_hbm_measured_copy"] = st["gbs"] / peaks["hbm_copy_gbs"]
         st["traffic"] = read_traffic(cfg.name, kind)
         kernels[kind] = st
     st = stats_ms(brackets["mse"])
@@ -361,6 +372,8 @@ def main():
         st.update({"bytes_per_launch": harness.mse_bytes(cfg),
                    "gbs": harness.mse_bytes(cfg) / (st["mean_ms"] * 1e-3) / 1e9})
         st["frac_hbm"] = st["gbs"] / PEAK_HBM_GBS
+        if peaks:
+            st["frac_hbm_measured_read"] = st["gbs"] / peaks["hbm_read_gbs"]
         st["traffic"] = read_traffic(cfg.name, "mse")
         kernels["mse"] = st
 
@@ -377,6 +390,9 @@ def main():
                 "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
                 "kernel": f"spatial_kernel<{cfg.D}>",
                 "algorithmic_flops_per_launch": kernels[dom]["flops_per_launch"]}
+    if peaks and cfg.dtype == "bf16":
+        roofline["measured_peak"] = peaks["mfma_bf16_tflops"]
+        roofline["frac_measured_peak"] = ach / peaks["mfma_bf16_tflops"]
 
     out = {
         "metric": METRIC,
@@ -405,6 +421,7 @@ def main():
         "pab_off_tflops": (flops_off / (off_ms * 1e-3) / 1e12) if off_ms else None,
         "kernels": kernels,
         "roofline": roofline,
+        "measured_peaks": peaks,
     }
     if args.module_config:
         out["module"] = module_leg(args.module_config, args.module_steps, dev, stream)

@@ -33,6 +33,7 @@ SOURCES = [
     "cross.hip",
     "temporal.hip",
     "proj.hip",
+    "peaks.hip",
 ]
 
 # Packed fp32 instructions are disabled for all device code on purpose.

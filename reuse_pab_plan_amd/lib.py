@@ -47,6 +47,16 @@ EXPORTED = (
     "pab_version",
 )
 
+# Measurement helpers (include/pab_peaks.h): microbenchmarks for the roofline
+# denominators, not part of the method.
+EXPORTED_PEAKS = (
+    "pab_peak_sink_bytes",
+    "pab_peak_copy",
+    "pab_peak_read",
+    "pab_peak_mfma_bf16",
+    "pab_peak_exp",
+)
+
 
 class PabError(RuntimeError):
     def __init__(self, fn, status, msg):
@@ -137,6 +147,16 @@ def load(path: str = LIB_PATH):
     lib.pab_last_error.restype = C.c_char_p
     lib.pab_version.argtypes = []
     lib.pab_version.restype = C.c_char_p
+    lib.pab_peak_sink_bytes.argtypes = []
+    lib.pab_peak_sink_bytes.restype = sz
+    lib.pab_peak_copy.argtypes = [vp, vp, sz, vp]
+    lib.pab_peak_copy.restype = C.c_int
+    lib.pab_peak_read.argtypes = [vp, sz, vp, sz, vp]
+    lib.pab_peak_read.restype = C.c_int
+    for name in ("pab_peak_mfma_bf16", "pab_peak_exp"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i32, vp, sz, C.POINTER(C.c_double), vp]
+        fn.restype = C.c_int
     _lib = lib
     return lib
 
@@ -301,3 +321,54 @@ def pab_step_dispatch(desc: StepDesc, step: int):
     st = load().pab_step_dispatch(C.byref(desc), step, C.byref(mask), outs)
     _check("pab_step_dispatch", st)
     return mask.value, [outs[a] for a in range(desc.num_types)]
+
+
+# ------------------------------------------------------------ measurement aids
+
+def measure_peaks(device=None, stream=None):
+    """Sustained peaks of this GPU from the pab_peak_* microbenchmarks, each
+    the best of a few launches timed with HIP events on ``stream``: HBM copy
+    (read + write) and read in GB/s over buffers rotated past the 256 MB
+    Infinity Cache, bf16 MFMA in TFLOP/s, v_exp_f32 in G/s."""
+    import torch
+
+    L = load()
+    dev = device or torch.device("cuda:0")
+    st = stream or torch.cuda.current_stream(dev)
+    sp = C.c_void_p(st.cuda_stream)
+    sink = torch.empty(int(L.pab_peak_sink_bytes()), dtype=torch.uint8, device=dev)
+    nbuf, nbytes = 4, 256 << 20
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2 * nbuf)]
+    for b in bufs:
+        b.fill_(1)
+
+    def best(launch, n=6):
+        ts = []
+        for i in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            launch(i)
+            e1.record(st)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts[1:])
+
+    out = {}
+    t = best(lambda i: _check("pab_peak_copy", L.pab_peak_copy(
+        C.c_void_p(bufs[i % nbuf].data_ptr()), C.c_void_p(bufs[nbuf + i % nbuf].data_ptr()),
+        nbytes, sp)))
+    out["hbm_copy_gbs"] = 2 * nbytes / t / 1e9
+    t = best(lambda i: _check("pab_peak_read", L.pab_peak_read(
+        C.c_void_p(bufs[i % (2 * nbuf)].data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
+        sink.numel(), sp)))
+    out["hbm_read_gbs"] = nbytes / t / 1e9
+    work = C.c_double(0.0)
+    t = best(lambda i: _check("pab_peak_mfma_bf16", L.pab_peak_mfma_bf16(
+        2048, C.c_void_p(sink.data_ptr()), sink.numel(), C.byref(work), sp)))
+    out["mfma_bf16_tflops"] = work.value / t / 1e12
+    t = best(lambda i: _check("pab_peak_exp", L.pab_peak_exp(
+        2048, C.c_void_p(sink.data_ptr()), sink.numel(), C.byref(work), sp)))
+    out["exp_gps"] = work.value / t / 1e9
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return out

@@ -18,8 +18,11 @@ HEADER = os.path.join(ROOT, "include", "pab.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH), reason="libpab.so not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+PEAKS_HEADER = os.path.join(ROOT, "include", "pab_peaks.h")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pab_[a-z_0-9]+)\s*\(", text)))
 
@@ -28,9 +31,25 @@ def test_exports_every_declared_symbol():
     L = lib.load()
     names = declared_functions()
     assert set(names) == set(lib.EXPORTED)
-    for name in names:
+    peaks = declared_functions(PEAKS_HEADER)
+    assert set(peaks) == set(lib.EXPORTED_PEAKS)
+    for name in names + peaks:
         assert hasattr(L, name), name
     assert "gfx950" in lib.pab_version()
+
+
+def test_peak_helpers_validate_before_launch():
+    L = lib.load()
+    sink_bytes = int(L.pab_peak_sink_bytes())
+    assert sink_bytes >= 8192 * 4
+    work = C.c_double(0.0)
+    assert L.pab_peak_copy(None, C.c_void_p(0x1000), 1024, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_copy(C.c_void_p(0x1000), C.c_void_p(0x1008), 1024, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_copy(C.c_void_p(0x1000), C.c_void_p(0x1200), 1024, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_read(C.c_void_p(0x1000), 1000, C.c_void_p(0x100000), sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_read(C.c_void_p(0x1000), 1024, C.c_void_p(0x100000), 16, None) == lib.PAB_ERR_CAPACITY
+    assert L.pab_peak_mfma_bf16(0, C.c_void_p(0x100000), sink_bytes, C.byref(work), None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_exp(1, C.c_void_p(0x100000), 64, C.byref(work), None) == lib.PAB_ERR_CAPACITY
 
 
 @pytest.mark.parametrize("win", [(15, 85), (0, 100), (50, 50), (0, 0), (30, 60), (10, 90)])
