@@ -216,3 +216,28 @@ def test_dispatch_module_rejects_slot_scratch_overlap():
     mask = C.c_uint32(0)
     ptrs = (C.c_void_p * 1)()
     assert lib.load().pab_step_dispatch(C.byref(d), 0, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG
+
+
+def test_projection_validation_codes():
+    # pab_proj_in / pab_proj_out: bf16 only, C = H*D a multiple of 32,
+    # 1..3 outputs, no aliasing; checked on the host before any launch.
+    L = lib.load()
+    pin, pout = L.pab_proj_in, L.pab_proj_out
+    X, W, Y0, Y1, Y2 = (C.c_void_p(a) for a in (0x1000000, 0x2000000, 0x3000000, 0x4000000,
+                                                 0x5000000))
+    ok_args = (1, 2, 10, 4, 64)  # B, F, S, H, D  (C = 256)
+    assert pin(X, W, Y0, Y1, Y2, 0, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pin(X, W, Y0, Y1, Y2, 4, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pin(X, W, Y0, None, Y2, 3, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pin(X, W, Y0, Y1, Y2, 3, *ok_args, lib.PAB_F32, None) == lib.PAB_ERR_UNSUPPORTED
+    assert pin(X, W, Y0, Y1, Y2, 3, 1, 2, 10, 3, 40, lib.PAB_BF16, None) == lib.PAB_ERR_UNSUPPORTED
+    assert "multiple of 32" in lib.pab_last_error()
+    assert pin(X, W, Y0, Y0, Y2, 3, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pin(X, W, X, Y1, Y2, 3, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pin(C.c_void_p(0x1000008), W, Y0, Y1, Y2, 3, *ok_args, lib.PAB_BF16, None) == \
+        lib.PAB_ERR_INVALID_ARG
+    assert pin(X, W, Y0, Y1, Y2, 3, 0, 2, 10, 4, 64, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pout(X, W, None, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pout(X, W, X, *ok_args, lib.PAB_BF16, None) == lib.PAB_ERR_INVALID_ARG
+    assert pout(X, W, Y0, *ok_args, lib.PAB_F32, None) == lib.PAB_ERR_UNSUPPORTED
+    assert pout(X, W, Y0, 1, 2, 10, 4, 60, lib.PAB_BF16, None) == lib.PAB_ERR_UNSUPPORTED

@@ -67,6 +67,9 @@ SPATIAL_CASES = [
     (1, 2, 2, 33, 16, "bf16"),
     (1, 4, 4, 64, 64, "f32"),       # tiny-config shape
     (1, 2, 2, 130, 72, "f32"),
+    (1, 2, 3, 1, 72, "bf16"),       # one token: the output is V
+    (1, 1, 1, 2, 64, "bf16"),
+    (1, 1, 2, 1, 64, "f32"),
 ]
 
 
@@ -93,6 +96,9 @@ TEMPORAL_CASES = [
     (1, 1, 17, 5, 8, "bf16"),
     (1, 4, 4, 64, 64, "f32"),       # tiny-config shape
     (1, 2, 48, 9, 72, "f32"),
+    (1, 2, 1, 40, 72, "bf16"),      # one frame: the output is V
+    (1, 1, 2, 1, 64, "bf16"),       # one token position
+    (1, 1, 1, 3, 64, "f32"),
 ]
 
 
@@ -119,6 +125,9 @@ CROSS_CASES = [
     (1, 1, 1, 40, 33, 8, "bf16"),
     (1, 4, 4, 64, 16, 64, "f32"),      # tiny-config shape
     (1, 2, 2, 70, 120, 72, "f32"),
+    (1, 1, 2, 45, 1, 72, "bf16"),      # one text token: the output is its V row
+    (1, 2, 1, 1, 1, 64, "bf16"),       # one query, one text token
+    (1, 1, 1, 3, 1, 64, "f32"),
 ]
 
 
