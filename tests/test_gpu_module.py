@@ -189,3 +189,31 @@ def test_module_shapes(name, changes):
         _compare(_host(slot), _module_full(cfg, kind, x, w), label)
 
     _run(cfg, check)
+
+
+def test_module_drift_is_mse_of_module_outputs():
+    # The attention difference of a module trajectory (pab_attn_diff_mse
+    # after each recompute, as the harness runs it) is taken on what the
+    # cache holds: the module outputs of successive recomputes (PAB article,
+    # Figure 1 caption: the difference between steps measured by the MSE).
+    # Checked against the oracle MSE of the GPU's own outputs (exact up to
+    # fp64 summation order) on a PAB-off trajectory.
+    _need_gpu()
+    cfg = harness.CONFIGS["mod_small"]
+    dev = torch.device("cuda:0")
+    traj = harness.Trajectory(cfg, pab=False, device=dev, drift=True)
+    traj.inputs = harness.Inputs(cfg, traj.steps_needed(), device=dev)
+    kept = {}
+
+    def on_step(i, outs):
+        torch.cuda.synchronize()
+        for a in range(len(cfg.kinds)):
+            kept[(a, i)] = _host(traj.slot_tensor(0, a, outs[0][i][a])).copy()
+
+    traj.run(on_step=on_step)
+    torch.cuda.synchronize()
+    drift = traj.drift_out.cpu().numpy()
+    for a in range(len(cfg.kinds)):
+        for i in range(1, cfg.N):
+            want = oracle.mse(kept[(a, i)], kept[(a, i - 1)])
+            assert abs(drift[0, a, i] - want) <= 1e-9 * max(want, 1e-30), (a, i, drift[0, a, i], want)
