@@ -265,7 +265,11 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
  *                skips all three (PAB article, "Implementation").  q, k, v
  *                are then not read.
  *       x        module input, token-major [B, F*S, C], C = H*D
- *       x_text   PAB_CROSS: text tokens [B, L, C] (key/value projection)
+ *       x_text   PAB_CROSS: text tokens [B, L, C] (key/value projection), or
+ *                NULL when scratch[1], scratch[2] already hold the projected
+ *                text K/V [B, H, L, D] (text that does not change over the
+ *                steps, projected once, e.g. with pab_proj_in); w_kv is then
+ *                not read
  *       w_in     [3C, C] q/k/v projection (self types); PAB_CROSS: [C, C]
  *                query projection
  *       w_kv     PAB_CROSS: [2C, C] key/value projection of the text

@@ -33,15 +33,17 @@ int check_module(const pab_step_desc* d, const pab_type_desc& t) {
   void* slot[3] = {t.slot[0], nullptr, nullptr};
   int st;
   if (t.kind == PAB_CROSS) {
-    if (!t.x_text || !t.w_kv)
-      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: a cross module needs x_text and w_kv");
+    if (t.x_text && !t.w_kv)
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: a cross module with x_text needs w_kv");
     st = check_proj("pab_step_dispatch(proj q)", t.x, t.w_in, qkv, 1, t.B, t.F, t.S, t.H, t.D,
                     d->dtype, true);
     if (st) return st;
-    void* kv[3] = {t.scratch[1], t.scratch[2], nullptr};
-    st = check_proj("pab_step_dispatch(proj kv)", t.x_text, t.w_kv, kv, 2, t.B, 1, t.L, t.H, t.D,
-                    d->dtype, true);
-    if (st) return st;
+    if (t.x_text) {  // else scratch[1], scratch[2] already hold the projected text K/V
+      void* kv[3] = {t.scratch[1], t.scratch[2], nullptr};
+      st = check_proj("pab_step_dispatch(proj kv)", t.x_text, t.w_kv, kv, 2, t.B, 1, t.L, t.H,
+                      t.D, d->dtype, true);
+      if (st) return st;
+    }
     st = check_cross_attn(t.scratch[0], t.scratch[1], t.scratch[2], t.scratch[3], t.B, t.H,
                           (int64_t)t.F * t.S, t.L, t.D, d->dtype, d->softmax_scale, t.text_len);
   } else {
@@ -170,7 +172,8 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
         void* q1[3] = {t.scratch[0], nullptr, nullptr};
         void* kv[3] = {t.scratch[1], t.scratch[2], nullptr};
         st = run_proj_in(t.x, t.w_in, q1, 1, t.B, t.F, t.S, t.H, t.D, desc->stream);
-        if (!st) st = run_proj_in(t.x_text, t.w_kv, kv, 2, t.B, 1, t.L, t.H, t.D, desc->stream);
+        if (!st && t.x_text)
+          st = run_proj_in(t.x_text, t.w_kv, kv, 2, t.B, 1, t.L, t.H, t.D, desc->stream);
         if (!st)
           st = run_cross(t.scratch[0], t.scratch[1], t.scratch[2], t.scratch[3], t.B, t.H,
                          (int64_t)t.F * t.S, t.L, t.D, desc->dtype, desc->softmax_scale,

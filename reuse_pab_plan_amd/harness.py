@@ -237,6 +237,13 @@ class Trajectory:
         # (block, type): the dispatches run one after another on one stream.
         self.mod_scratch = ([torch.empty(cfg.video_shape, dtype=tdt, device=self.device)
                              for _ in range(4)] if cfg.module else None)
+        # Constant text (a module workload with const_text): the text K/V of
+        # each block are projected once per trajectory into buffers of their
+        # own, and the cross modules read them instead of projecting again.
+        self.text_kv = ([(torch.empty(cfg.text_shape, dtype=tdt, device=self.device),
+                          torch.empty(cfg.text_shape, dtype=tdt, device=self.device))
+                         for _ in range(cfg.blocks)]
+                        if cfg.module and cfg.const_text and "cross" in cfg.kinds else None)
         n = int(np.prod(cfg.video_shape))
         self.ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=self.device)
         self.drift_out = torch.zeros((cfg.blocks, self.T, cfg.N), dtype=torch.float64,
@@ -291,6 +298,7 @@ class Trajectory:
         brackets = {"attn": [[] for _ in range(self.T)], "mse": []}
         last = [[None] * self.T for _ in range(cfg.blocks)]
         mk = (lambda: torch.cuda.Event(enable_timing=True)) if events else None
+        text_done = set()  # blocks whose constant text K/V this run has projected
         with torch.cuda.stream(self.stream):
             for i in range(cfg.N if max_steps is None else min(max_steps, cfg.N)):
                 for b in range(cfg.blocks):
@@ -305,6 +313,14 @@ class Trajectory:
                             t[0].x_text = x[1].data_ptr() if len(x) > 1 else None
                             t[0].w_in, t[0].w_out = w_in.data_ptr(), w_out.data_ptr()
                             t[0].w_kv = w_kv.data_ptr() if w_kv is not None else None
+                            if self.text_kv is not None and len(x) > 1:
+                                tk, tv = self.text_kv[b]
+                                if b not in text_done:
+                                    lib.pab_proj_in(x[1], w_kv, [tk, tv], 1, cfg.L, cfg.H, cfg.D,
+                                                    stream=self.stream)
+                                    text_done.add(b)
+                                t[0].x_text = None
+                                t[0].scratch[1], t[0].scratch[2] = tk.data_ptr(), tv.data_ptr()
                         elif rec:
                             q, k, v = self.inputs.get(b, a, i)
                             t[0].q, t[0].k, t[0].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
