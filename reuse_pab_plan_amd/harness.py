@@ -137,6 +137,19 @@ def proj_flops(cfg: Config, kind: str) -> int:
     return 2 * C_ * C_ * 4 * tokens
 
 
+def cache_bytes(cfg: Config) -> int:
+    """HBM the broadcast cache needs: two output-sized slots per (block, type)."""
+    return 2 * cfg.blocks * len(cfg.kinds) * cfg.B * cfg.H * cfg.F * cfg.S * cfg.D * cfg.elem_bytes
+
+
+def check_capacity(need: int, free: int, what: str) -> None:
+    """Raise PAB_ERR_CAPACITY (as lib.PabError) when `need` bytes exceed the
+    `free` device bytes, before anything is allocated."""
+    if need > free:
+        raise lib.PabError(what, lib.PAB_ERR_CAPACITY,
+                           f"needs {need / 2**30:.2f} GiB of HBM, {free / 2**30:.2f} GiB free")
+
+
 def mse_bytes(cfg: Config) -> int:
     return 2 * cfg.B * cfg.H * cfg.F * cfg.S * cfg.D * cfg.elem_bytes
 
@@ -229,6 +242,12 @@ class Trajectory:
         self.T = len(cfg.kinds)
         tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         # Cache: two O-sized slots per (block, type), resident in HBM.
+        # The cache lives in HBM for the whole trajectory (two slots per
+        # block and type; 29.5 GB for the 28-block stack at 480p): check it
+        # fits before allocating it.
+        if self.device.type == "cuda":
+            check_capacity(cache_bytes(cfg), torch.cuda.mem_get_info(self.device)[0],
+                           f"broadcast cache of {cfg.name}")
         out_shape = (cfg.B, cfg.F * cfg.S, cfg.C) if cfg.module else cfg.video_shape
         self.slots = [[(torch.empty(out_shape, dtype=tdt, device=self.device),
                         torch.empty(out_shape, dtype=tdt, device=self.device))

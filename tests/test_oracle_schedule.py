@@ -132,3 +132,4 @@ def test_types_independent():
     for a, r in enumerate([2, 4, 6]):
         r1, s1, _ = schedule(30, [r])
         assert np.array_equal(rec[:, a], r1[:, 0]) and np.array_equal(src[:, a], s1[:, 0])
+
