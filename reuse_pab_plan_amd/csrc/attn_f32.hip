@@ -48,6 +48,16 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
   float m = -INFINITY;  // running max of scaled (log2-domain) scores
   float l = 0.f;        // running sum of exp2(score - m)
 
+  // Columns D..DMAX-1 of the tiles are never loaded but take part in the
+  // unrolled products (against zero q and unused accumulators): zero them
+  // once, so stale LDS contents (possibly NaN bit patterns) cannot leak in.
+  // The first barrier of the key loop orders these stores before any read.
+  for (int idx = threadIdx.x; idx < kTile * (DMAX - D); idx += kRows) {
+    const int r = idx / (DMAX - D), d = D + idx % (DMAX - D);
+    ks[r][d] = 0.f;
+    vs[r][d] = 0.f;
+  }
+
   for (int64_t k0 = 0; k0 < lay.lk; k0 += kTile) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < kTile * D; idx += kRows) {

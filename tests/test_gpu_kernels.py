@@ -300,3 +300,24 @@ def test_mse_exact_dyadic_shift():
     lib.pab_attn_diff_mse(x.cuda(), y.cuda(), out, ws)
     torch.cuda.synchronize()
     assert out.item() == 0.25
+
+
+@pytest.mark.parametrize("D", [72, 40, 8])
+def test_f32_path_ignores_stale_lds(D):
+    # The fp32 kernel's tiles have columns past D that are never loaded.  Run
+    # a bf16 spatial call over NaN inputs first, on every CU, so the LDS holds
+    # NaN bit patterns, then the fp32 call: its output must stay finite and
+    # match the oracle (regression test: those columns once read stale LDS).
+    dev = _dev()
+    junk = torch.full((1, 8, 64, 1590, 72), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(junk)
+    lib.pab_attn_spatial(junk, junk, junk, out)
+    case = (1, 2, 2, 130, D, "f32")
+    q, k, v = inputs(case[:5], "f32", 31, 0)
+    ref = oracle.spatial(q, k, v)
+    qd, kd, vd = to_dev(q, k, v)
+    o = torch.empty_like(qd)
+    lib.pab_attn_spatial(qd, kd, vd, o)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    assert_close(o, ref, "f32", f"spatial {case} after NaN LDS")
