@@ -150,11 +150,14 @@ static float resolve_scale(float scale, int32_t D) {
 }
 
 int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
-                int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream) {
+                int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream,
+                const DiffOut* diff) {
   const float c = resolve_scale(scale, D);
   hipError_t e;
+  if (diff && diff->nparts) *diff->nparts = 0;
   if (dtype == PAB_BF16) {
-    e = launch_spatial_bf16(q, k, v, o, (int64_t)B * H * F, S, D, c, (hipStream_t)stream);
+    e = launch_spatial_bf16(q, k, v, o, (int64_t)B * H * F, S, D, c, diff ? *diff : DiffOut{},
+                            (hipStream_t)stream);
   } else {
     SeqLayout lay{(int64_t)B * H * F, 1, (int64_t)S * D, 0, D, (int64_t)S * D, 0, D, S, S};
     e = launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lay, D, c,
@@ -164,11 +167,14 @@ int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B,
 }
 
 int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
-                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream) {
+                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream,
+                 const DiffOut* diff) {
   const float c = resolve_scale(scale, D);
   hipError_t e;
+  if (diff && diff->nparts) *diff->nparts = 0;
   if (dtype == PAB_BF16) {
-    e = launch_temporal_bf16(q, k, v, o, (int64_t)B * H, F, S, D, c, (hipStream_t)stream);
+    e = launch_temporal_bf16(q, k, v, o, (int64_t)B * H, F, S, D, c, diff ? *diff : DiffOut{},
+                             (hipStream_t)stream);
   } else {
     const int64_t fs = (int64_t)F * S * D;
     SeqLayout lay{(int64_t)B * H * S, S, fs, D, (int64_t)S * D, fs, D, (int64_t)S * D, F, F};
@@ -180,8 +186,9 @@ int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B
 
 int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B, int32_t H,
               int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale,
-              const int32_t* text_len, void* stream) {
+              const int32_t* text_len, void* stream, const DiffOut* diff) {
   const float c = resolve_scale(scale, D);
+  if (diff && diff->nparts) *diff->nparts = 0;
   bool full = true;
   if (text_len)
     for (int32_t b = 0; b < B; ++b) full = full && text_len[b] == L;
@@ -200,7 +207,8 @@ int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B,
     char* ob = (char*)o + qo;
     hipError_t e;
     if (dtype == PAB_BF16) {
-      e = launch_cross_bf16(qb, kb, vb, ob, nbh, Nq, len, L, D, c, (hipStream_t)stream);
+      e = launch_cross_bf16(qb, kb, vb, ob, nbh, Nq, len, L, D, c,
+                            (full && diff) ? *diff : DiffOut{}, (hipStream_t)stream);
     } else {
       SeqLayout lay{nbh, 1, Nq * D, 0, D, (int64_t)L * D, 0, D, Nq, len};
       e = launch_attn_f32((const float*)qb, (const float*)kb, (const float*)vb, (float*)ob, lay, D,
@@ -215,6 +223,11 @@ int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out,
             void* stream) {
   hipError_t e = launch_mse(a, b, n, dtype, out, (double*)ws, (hipStream_t)stream);
   return e == hipSuccess ? ok() : device_error("pab_attn_diff_mse launch", e);
+}
+
+int run_mse_final(const double* partials, int nparts, int64_t n, double* out, void* stream) {
+  hipError_t e = launch_mse_final(partials, nparts, n, out, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : device_error("pab_step_dispatch(attention difference)", e);
 }
 
 
@@ -327,10 +340,14 @@ int pab_proj_out(const void* o, const void* w, void* y, int32_t B, int32_t F, in
 
 size_t pab_mse_workspace_bytes(int64_t n) {
   if (n < 1) return 0;
-  // Enough partials for either dtype's grid, rounded to 256 bytes.
-  const int blocks = mse_num_blocks(n, PAB_F32) > mse_num_blocks(n, PAB_BF16)
-                         ? mse_num_blocks(n, PAB_F32)
-                         : mse_num_blocks(n, PAB_BF16);
+  // Enough partials for either dtype's grid, and for one per block of the
+  // attention kernels that fuse the difference into their output pass (the
+  // dispatcher falls back to the separate reduction when a launch has more
+  // blocks than this holds), rounded to 256 bytes.
+  int64_t blocks = mse_num_blocks(n, PAB_F32) > mse_num_blocks(n, PAB_BF16)
+                       ? mse_num_blocks(n, PAB_F32)
+                       : mse_num_blocks(n, PAB_BF16);
+  if (n / 1024 + 64 > blocks) blocks = n / 1024 + 64;
   return ((size_t)blocks * sizeof(double) + 255) / 256 * 256;
 }
 

@@ -7,6 +7,7 @@
 #include <string>
 
 #include "../../include/pab.h"
+#include "launch.hpp"
 
 namespace pab {
 
@@ -32,15 +33,21 @@ int check_mse(const void* a, const void* b, int64_t n, int32_t dtype, const doub
               const void* ws, size_t ws_bytes);
 
 // Launch without re-validating (arguments already checked).
+// diff (optional, bf16 only): fuse the attention difference against
+// diff->prev into the output pass when it fits (see DiffOut); cross
+// attention fuses it only when every text token is real (one launch).
 int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
-                int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream);
+                int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream,
+                const DiffOut* diff = nullptr);
 int run_temporal(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
-                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream);
+                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream,
+                 const DiffOut* diff = nullptr);
 int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B, int32_t H,
               int64_t Nq, int32_t L, int32_t D, int32_t dtype, float scale,
-              const int32_t* text_len, void* stream);
+              const int32_t* text_len, void* stream, const DiffOut* diff = nullptr);
 int run_mse(const void* a, const void* b, int64_t n, int32_t dtype, double* out, void* ws,
             void* stream);
+int run_mse_final(const double* partials, int nparts, int64_t n, double* out, void* stream);
 
 // Projections around an attention (bf16).  in = true: input projection
 // (x token-major [B, F*S, C] -> n_out head-major tensors); false: output

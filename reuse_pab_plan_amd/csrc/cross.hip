@@ -22,6 +22,9 @@
 //     requests, no staging registers), the next tile's loads running while
 //     the current one computes; the tile's output is staged row-major in the
 //     same stage and written with lane-contiguous 16-byte stores.
+//   * With a previous output to compare against (the attention difference),
+//     its tile comes in beside the query tile, into a second ring, and the
+//     copy-out accumulates the squared differences.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -106,19 +109,25 @@ struct Geo {
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
 };
 
-template <int D, int NKB>
-__global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restrict__ Q,
+template <int D, int NKB, bool DIFF>
+__global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf16* __restrict__ Q,
                                                            const bf16* __restrict__ Kt,
                                                            const bf16* __restrict__ Vt,
                                                            bf16* __restrict__ O, int64_t nq, int L, int Lrows,
                                                            int tiles_per_block, int blocks_per_bh,
-                                                           int nblocks, float c) {
+                                                           int nblocks, float c,
+                                                           const bf16* __restrict__ P,
+                                                           double* __restrict__ partials) {
   using G = Geo<D, NKB>;
+  // Direct loads per query tile: the tile, and the previous output's tile.
+  constexpr int QJ = DIFF ? 2 * G::NQJ : G::NQJ;
   __shared__ __attribute__((aligned(16))) bf16 ks[G::KROWS * G::KS];
   __shared__ __attribute__((aligned(16))) bf16 vs[G::VROWS * G::VS + G::VSLACK];
   // Per-wave two-stage ring of query tiles (each stage later holds the
   // tile's output, row-major).
   __shared__ __attribute__((aligned(16))) bf16 qstage[kWaves][2][G::QSTAGE];
+  // Previous output tiles (attention difference only).
+  __shared__ __attribute__((aligned(16))) bf16 pstage[DIFF ? kWaves : 1][2][DIFF ? G::QSTAGE : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -128,6 +137,8 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
   const int chunk = logical % blocks_per_bh;
   const bf16* __restrict__ Qh = Q + (int64_t)bh * nq * D;
   bf16* __restrict__ Oh = O + (int64_t)bh * nq * D;
+  const bf16* __restrict__ Ph = DIFF ? P + (int64_t)bh * nq * D : nullptr;
+  double dsum = 0.0;
   // Text rows of (b, h) are Lrows apart; the first L of them are real.
   const bf16* __restrict__ Kh = Kt + (int64_t)bh * Lrows * D;
   const bf16* __restrict__ Vh = Vt + (int64_t)bh * Lrows * D;
@@ -194,11 +205,12 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
   // Q padding word at d = D (1 in its low half) when the bias column is used.
   const uint32_t qpad_word = G::BIAS ? 0x00003F80u : 0u;
 
-  // Direct loads of query tile `tile` into stage `st` (LDS byte address):
-  // lane l of load j copies tile bytes [1024 j + 16 l, +16), clamped to the
-  // tile's last valid 16 bytes (rows past nq re-read it: finite values whose
-  // outputs are not stored).
-  auto issue_q = [&](int tile, uint32_t st) {
+  // Direct loads of query tile `tile` into stage `st` (LDS byte address),
+  // and of the previous output's tile into stage `pst` when DIFF: lane l of
+  // load j copies tile bytes [1024 j + 16 l, +16), clamped to the tile's last
+  // valid 16 bytes (rows past nq re-read it: finite values whose outputs are
+  // not stored).
+  auto issue_q = [&](int tile, uint32_t st, uint32_t pst) {
     const int64_t rows_left = nq - (int64_t)tile * 32;
     const uint32_t valid = (uint32_t)((rows_left >= 32 ? 32 : rows_left) * D * 2);
     const bf16* tb = Qh + (int64_t)tile * 32 * D;
@@ -209,11 +221,20 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
       // Lanes past the stage stay idle (their LDS bytes are not written).
       if (j + 1 < G::NQJ || pos < (uint32_t)(32 * D * 2)) dma16(tb, off, st + (uint32_t)(j * 1024));
     }
+    if (DIFF) {
+      const bf16* pb = Ph + (int64_t)tile * 32 * D;
+#pragma unroll
+      for (int j = 0; j < G::NQJ; ++j) {
+        const uint32_t pos = (uint32_t)(j * 1024 + lane * 16);
+        const uint32_t off = min(pos, valid - 16u);
+        if (j + 1 < G::NQJ || pos < (uint32_t)(32 * D * 2)) dma16(pb, off, pst + (uint32_t)(j * 1024));
+      }
+    }
   };
 
   // One 32-row query tile against the text keys: full-row softmax,
   // O = P V / sum(P) on the MFMA, row-major staging, coalesced stores.
-  auto compute = [&](bf16* ost, int tile) {
+  auto compute = [&](bf16* ost, const bf16* pst, int tile) {
     // Q^T operand: lane (row l32, half h) holds d = ds*16 + h*8 .. +7.
     const uint32_t qlane = (uint32_t)(uintptr_t)LDS_PTR(void, ost) + (uint32_t)((l32 * D + h * 8) * 2);
     u32x4 q[G::ND];
@@ -303,8 +324,15 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
 #pragma unroll
     for (int i = 0; i < (kOutChunks + kWave - 1) / kWave; ++i) {
       const int ch = i * kWave + lane;
-      if (ch < valid_chunks)
-        *reinterpret_cast<uint4*>(obase + ch * 8) = *reinterpret_cast<const uint4*>(&ost[ch * 8]);
+      if (ch < valid_chunks) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&ost[ch * 8]);
+        *reinterpret_cast<uint4*>(obase + ch * 8) = w;
+        if (DIFF) {
+          const uint4 pw = *reinterpret_cast<const uint4*>(&pst[ch * 8]);
+          dsum += sqdiff_bf16x2(w.x, pw.x) + sqdiff_bf16x2(w.y, pw.y) + sqdiff_bf16x2(w.z, pw.z) +
+                  sqdiff_bf16x2(w.w, pw.w);
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -312,35 +340,49 @@ __global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restri
   // This wave's tiles: t_begin + wave, + 4, + 8, ...; tile k of the wave
   // sits in stage k % 2, and the next tile's loads run while one computes.
   // vmcnt accounting: after the loads of tile k come the stores of tile k-1
-  // (NOST instructions, always a full tile) and the loads of tile k+1 (NQJ).
+  // (NOST instructions, always a full tile) and the loads of tile k+1 (QJ).
   const uint32_t st0 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][0]);
   const uint32_t st1 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][1]);
+  const uint32_t ps0 = DIFF ? (uint32_t)(uintptr_t)LDS_PTR(void, pstage[DIFF ? wave : 0][0]) : 0u;
+  const uint32_t ps1 = DIFF ? (uint32_t)(uintptr_t)LDS_PTR(void, pstage[DIFF ? wave : 0][1]) : 0u;
   const int first = t_begin + wave;
   const int n = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
-  if (n > 0) issue_q(first, st0);
+  if (n > 0) issue_q(first, st0, ps0);
   for (int k = 0; k < n; ++k) {
     const int tile = first + k * kWaves;
     const bool more = k + 1 < n;
-    if (more) issue_q(tile + kWaves, (k & 1) ? st0 : st1);
+    if (more) issue_q(tile + kWaves, (k & 1) ? st0 : st1, (k & 1) ? ps0 : ps1);
     if (k >= 1) {
-      if (more) wait_vmcnt<G::NOST + G::NQJ>(); else wait_vmcnt<G::NOST>();
+      if (more) wait_vmcnt<G::NOST + QJ>(); else wait_vmcnt<G::NOST>();
     } else {
-      if (more) wait_vmcnt<G::NQJ>(); else wait_vmcnt<0>();
+      if (more) wait_vmcnt<QJ>(); else wait_vmcnt<0>();
     }
-    compute(qstage[wave][k & 1], tile);
+    compute(qstage[wave][k & 1], DIFF ? pstage[DIFF ? wave : 0][k & 1] : nullptr, tile);
+  }
+  if (DIFF) {
+    __syncthreads();  // every wave is done with its ring: reuse it for the sum
+    const double s = block_sum_f64<kWaves>(dsum, reinterpret_cast<double*>(&qstage[0][0][0]));
+    if (tid == 0) partials[blockIdx.x] = s;
   }
 }
 
-template <int D, int NKB>
+template <int D, int NKB, bool DIFF>
 hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
-                     int64_t nq, int L, int Lrows, float c, hipStream_t stream) {
+                     int64_t nq, int L, int Lrows, float c, const DiffOut& diff,
+                     hipStream_t stream) {
   // Size the grid to whole waves of resident blocks (as many per CU as the
   // LDS allows, at most 2, on 256 CUs): each (b, h) gets the same number of
   // blocks, as many as keep the grid within the fewest waves that leave at
   // most 96 query tiles per block (the text K/V load is amortized over them).
   using G = Geo<D, NKB>;
   constexpr int kLdsBytes = (G::KROWS * G::KS + G::VROWS * G::VS + G::VSLACK) * 2 +
-                            kWaves * 2 * G::QSTAGE * 2;
+                            (DIFF ? 2 : 1) * kWaves * 2 * G::QSTAGE * 2;
+  if constexpr (DIFF && kLdsBytes > 160 * 1024) {
+    // No room for the previous output's ring (wide heads with many text
+    // tokens): plain launch, nparts stays 0 and the caller takes the
+    // difference in a separate pass.
+    return launch_dk<D, NKB, false>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
+  } else {
   constexpr int kPerCu = (160 * 1024) / kLdsBytes >= 2 ? 2 : 1;
   const int64_t ntiles = (nq + 31) / 32;
   const int64_t wave_blocks = 256 * kPerCu;
@@ -356,30 +398,48 @@ hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int
   blocks_per_bh = (ntiles + tiles_per_block - 1) / tiles_per_block;
   const int64_t nblocks = blocks_per_bh * nbh;
   if (nblocks > 0x7fffffff || ntiles > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((cross_kernel<D, NKB>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)kt, (const bf16*)vt, (bf16*)o, nq, L, Lrows,
-                     (int)tiles_per_block, (int)blocks_per_bh, (int)nblocks, c);
+  if (DIFF) {
+    if (nblocks > diff.capacity) return hipErrorInvalidConfiguration;  // caller checks first
+    *diff.nparts = (int)nblocks;
+  }
+  hipLaunchKernelGGL((cross_kernel<D, NKB, DIFF>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+                     stream, (const bf16*)q, (const bf16*)kt, (const bf16*)vt, (bf16*)o, nq, L,
+                     Lrows, (int)tiles_per_block, (int)blocks_per_bh, (int)nblocks, c,
+                     DIFF ? (const bf16*)diff.prev : nullptr, DIFF ? diff.partials : nullptr);
   return hipGetLastError();
+  }
 }
 
+template <int D, bool DIFF>
+hipError_t launch_dd(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
+                     int64_t nq, int L, int Lrows, float c, const DiffOut& diff,
+                     hipStream_t stream) {
+  if (L <= 32) return launch_dk<D, 1, DIFF>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
+  if (L <= 64) return launch_dk<D, 2, DIFF>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
+  return launch_dk<D, 4, DIFF>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
+}
+
+// The fused difference needs one partial per block: at most the blocks of
+// the grid, which launch_dk sizes to at most ntiles per (b, h).
 template <int D>
 hipError_t launch_d(const void* q, const void* kt, const void* vt, void* o, int64_t nbh, int64_t nq,
-                    int L, int Lrows, float c, hipStream_t stream) {
-  if (L <= 32) return launch_dk<D, 1>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
-  if (L <= 64) return launch_dk<D, 2>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
-  return launch_dk<D, 4>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
+                    int L, int Lrows, float c, const DiffOut& diff, hipStream_t stream) {
+  const int64_t max_blocks = nbh * ((nq + 31) / 32);
+  if (diff.prev && diff.nparts && max_blocks <= diff.capacity)
+    return launch_dd<D, true>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
+  return launch_dd<D, false>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
 }
 
 }  // namespace
 
 hipError_t launch_cross_bf16(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
                              int64_t nq, int L, int Lrows, int D, float scale,
-                             hipStream_t stream) {
+                             const DiffOut& diff, hipStream_t stream) {
   const float c = scale * kLog2e;
   switch (D) {
 #define PAB_CASE(d) \
   case d:           \
-    return launch_d<d>(q, kt, vt, o, nbh, nq, L, Lrows, c, stream);
+    return launch_d<d>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
     PAB_CASE(8) PAB_CASE(16) PAB_CASE(24) PAB_CASE(32) PAB_CASE(40) PAB_CASE(48) PAB_CASE(56)
     PAB_CASE(64) PAB_CASE(72) PAB_CASE(80) PAB_CASE(88) PAB_CASE(96) PAB_CASE(104) PAB_CASE(112)
     PAB_CASE(120) PAB_CASE(128)

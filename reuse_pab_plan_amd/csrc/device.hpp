@@ -74,6 +74,33 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
 }
 
+// Sum over the two bf16 pairs of (a_i - b_i)^2, the differences formed and
+// squared in fp64 (the attention difference of two stored outputs).
+__device__ __forceinline__ double sqdiff_bf16x2(uint32_t a, uint32_t b) {
+  const double d0 = (double)bf16_bits_to_float(a & 0xFFFFu) - (double)bf16_bits_to_float(b & 0xFFFFu);
+  const double d1 = (double)__builtin_bit_cast(float, a & 0xFFFF0000u) -
+                    (double)__builtin_bit_cast(float, b & 0xFFFF0000u);
+  return __builtin_fma(d1, d1, d0 * d0);
+}
+
+// Block-wide fp64 sum in a fixed order (butterfly within each wave, then the
+// waves in index order); the result is valid in thread 0.  `red` is an LDS
+// array of WAVES doubles.  Every thread of the block must call it.
+template <int WAVES>
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += red[w];
+  }
+  return s;
+}
+
 // Lane exchange with the lane 32 positions away (the other half-wave).
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 

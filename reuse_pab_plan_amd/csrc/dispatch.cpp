@@ -165,6 +165,20 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
     if (!desc->recompute[(size_t)step * nt + a]) continue;  // broadcast: no work at all
     mask |= 1u << a;
     int st;
+    // The attention difference against the previous computation of this
+    // type (when asked for): bf16 attention kernels fold it into their output
+    // pass (partial sums per block in the workspace, then one final
+    // reduction); otherwise a separate MSE pass follows.
+    const bool want_diff = two && t.drift && count[a] >= 2;
+    const void* prev = want_diff ? t.slot[count[a] & 1] : nullptr;
+    int nparts = 0;
+    DiffOut diff;
+    if (want_diff && !t.x && desc->dtype == PAB_BF16) {
+      diff.prev = prev;
+      diff.partials = (double*)desc->workspace;
+      diff.capacity = (int64_t)(desc->workspace_bytes / sizeof(double));
+      diff.nparts = &nparts;
+    }
     if (t.x) {
       // The whole attention module: projections around the attention.
       void* qkv[3] = {t.scratch[0], t.scratch[1], t.scratch[2]};
@@ -192,23 +206,25 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
     switch (t.kind) {
       case PAB_SPATIAL:
         st = run_spatial(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
-                         desc->softmax_scale, desc->stream);
+                         desc->softmax_scale, desc->stream, &diff);
         break;
       case PAB_TEMPORAL:
         st = run_temporal(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
-                          desc->softmax_scale, desc->stream);
+                          desc->softmax_scale, desc->stream, &diff);
         break;
       default:
         st = run_cross(t.q, t.k, t.v, cur, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D, desc->dtype,
-                       desc->softmax_scale, t.text_len, desc->stream);
+                       desc->softmax_scale, t.text_len, desc->stream, &diff);
         break;
     }
     }
     if (st) return st;
-    if (two && t.drift && count[a] >= 2) {
-      const void* prev = t.slot[count[a] & 1];
-      st = run_mse(cur, prev, (int64_t)output_elems(t), desc->dtype, t.drift + step,
-                   desc->workspace, desc->stream);
+    if (want_diff) {
+      st = nparts > 0
+               ? run_mse_final((const double*)desc->workspace, nparts, (int64_t)output_elems(t),
+                               t.drift + step, desc->stream)
+               : run_mse(cur, prev, (int64_t)output_elems(t), desc->dtype, t.drift + step,
+                         desc->workspace, desc->stream);
       if (st) return st;
     }
   }

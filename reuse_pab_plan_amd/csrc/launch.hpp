@@ -21,14 +21,29 @@ struct SeqLayout {
   int64_t lq, lk;
 };
 
+// Optional fused attention difference: with `prev` set (the previous output
+// of the same call, same layout as o) and the launch's block count within
+// `capacity`, every block writes sum (o - prev)^2 over its outputs (fp64) to
+// partials[block] and *nparts receives the block count; otherwise *nparts
+// is 0 and nothing extra is computed.
+struct DiffOut {
+  const void* prev = nullptr;
+  double* partials = nullptr;
+  int64_t capacity = 0;
+  int* nparts = nullptr;
+};
+
 hipError_t launch_spatial_bf16(const void* q, const void* k, const void* v, void* o, int64_t nseq,
-                               int S, int D, float scale, hipStream_t stream);
+                               int S, int D, float scale, const DiffOut& diff,
+                               hipStream_t stream);
 hipError_t launch_temporal_bf16(const void* q, const void* k, const void* v, void* o, int64_t nbh,
-                                int F, int S, int D, float scale, hipStream_t stream);
+                                int F, int S, int D, float scale, const DiffOut& diff,
+                                hipStream_t stream);
 // Text K/V rows of one (b, h) are Lrows apart; the first L of them are real
 // (L <= Lrows, the rest are padding and take no part).
 hipError_t launch_cross_bf16(const void* q, const void* kt, const void* vt, void* o, int64_t nbh,
-                             int64_t nq, int L, int Lrows, int D, float scale, hipStream_t stream);
+                             int64_t nq, int L, int Lrows, int D, float scale, const DiffOut& diff,
+                             hipStream_t stream);
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o,
                            const SeqLayout& lay, int D, float scale, hipStream_t stream);
 
@@ -43,5 +58,8 @@ hipError_t launch_proj_bf16(const void* x, const void* w, void* const out[3], in
 int mse_num_blocks(int64_t n, int dtype);
 hipError_t launch_mse(const void* a, const void* b, int64_t n, int dtype, double* out,
                       double* partials, hipStream_t stream);
+// out = (sum of partials[0..nparts), in a fixed order) / n.
+hipError_t launch_mse_final(const double* partials, int nparts, int64_t n, double* out,
+                            hipStream_t stream);
 
 }  // namespace pab

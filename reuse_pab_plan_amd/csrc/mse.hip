@@ -108,8 +108,19 @@ __global__ __launch_bounds__(kThreads) void mse_partial_kernel(const u32x4* __re
 __global__ __launch_bounds__(kThreads) void mse_final_kernel(const double* __restrict__ partials,
                                                             int nparts, int64_t n,
                                                             double* __restrict__ out) {
+  // Eight loads in flight per thread; the order of the additions depends on
+  // nparts alone, so the result is the same on every call.
+  constexpr int U = 8;
   double acc = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) acc += partials[i];
+  int i = threadIdx.x;
+  for (; i + (U - 1) * kThreads < nparts; i += U * kThreads) {
+    double x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = partials[i + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += x[u];
+  }
+  for (; i < nparts; i += kThreads) acc += partials[i];
   const double s = block_sum(acc);
   if (threadIdx.x == 0) *out = s / (double)n;
 }
@@ -140,6 +151,12 @@ hipError_t launch_mse(const void* a, const void* b, int64_t n, int dtype, double
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(kThreads), 0, stream, partials, blocks, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mse_final(const double* partials, int nparts, int64_t n, double* out,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(kThreads), 0, stream, partials, nparts, n, out);
   return hipGetLastError();
 }
 

@@ -144,7 +144,9 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
                                                              const bf16* __restrict__ K,
                                                              const bf16* __restrict__ V,
                                                              bf16* __restrict__ O, int S, int nqt,
-                                                             int nblocks, float c) {
+                                                             int nblocks, float c,
+                                                             const bf16* __restrict__ P,
+                                                             double* __restrict__ partials) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) bf16 ring[G::NST * G::STAGE];
 
@@ -159,6 +161,10 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   const bf16* __restrict__ Ks = K + base;
   const bf16* __restrict__ Vs = V + base;
   bf16* __restrict__ Os = O + base;
+  // P (optional): the previous output of the same call, for the attention
+  // difference -- each block adds up (O - P)^2 over the elements it writes.
+  const bf16* __restrict__ Ps = P ? P + base : nullptr;
+  double dsum = 0.0;
 
   // Direct-load plan of this wave: loads j = wave + 4i.  Load j covers stage
   // slots 64 j .. 64 j + 63; slot s of the K (V) rows is chunk
@@ -424,10 +430,57 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
       unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA, mA);
     }
 
+    // The output rows, normalized by the denominator in row D of O^T.
+    auto out_word = [&](int qb, int nb, int g, float inv) __attribute__((always_inline)) {
+      return make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
+                        pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
+    };
+    float inv[QBX];
 #pragma unroll
     for (int qb = 0; qb < QBX; ++qb) {
       const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
-      const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+      inv[qb] = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+    }
+    if (Ps) {
+      // Attention difference against the previous output: every word of it
+      // is requested before the first is used, so the block waits for one
+      // load latency rather than one per word.
+      uint2 pw[QBX][G::NB][4];
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) {
+        const int qrow = qrow0 + qb * 32 + l32;
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = nb * 32 + g * 8 + h * 4;
+            pw[qb][nb][g] = make_uint2(0u, 0u);
+            if (d0 < D && qrow < S)
+              pw[qb][nb][g] = *reinterpret_cast<const uint2*>(Ps + (size_t)qrow * D + d0);
+          }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) {
+        const int qrow = qrow0 + qb * 32 + l32;
+        if (qrow < S) {
+          bf16* orow = Os + (size_t)qrow * D;
+#pragma unroll
+          for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int d0 = nb * 32 + g * 8 + h * 4;
+              if (d0 < D) {
+                const uint2 w = out_word(qb, nb, g, inv[qb]);
+                *reinterpret_cast<uint2*>(orow + d0) = w;
+                dsum += sqdiff_bf16x2(w.x, pw[qb][nb][g].x) + sqdiff_bf16x2(w.y, pw[qb][nb][g].y);
+              }
+            }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QBX; ++qb) {
       const int qrow = qrow0 + qb * 32 + l32;
       if (qrow < S) {
         bf16* orow = Os + (size_t)qrow * D;
@@ -436,12 +489,7 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int d0 = nb * 32 + g * 8 + h * 4;
-            if (d0 < D) {
-              const uint2 w =
-                  make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
-                             pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
-              *reinterpret_cast<uint2*>(orow + d0) = w;
-            }
+            if (d0 < D) *reinterpret_cast<uint2*>(orow + d0) = out_word(qb, nb, g, inv[qb]);
           }
       }
     }
@@ -450,35 +498,44 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   // A sequence's last block usually holds fewer rows than the block covers;
   // when 32 rows per wave cover them, every wave takes one 32-row block
   // instead of leaving waves idle.
-  if constexpr (G::QB == 2) {
-    if (S - qt * G::BM <= kWaves * 32) {
-      run(std::integral_constant<int, 1>{});
-      return;
-    }
+  bool narrow = false;
+  if constexpr (G::QB == 2) narrow = S - qt * G::BM <= kWaves * 32;
+  if (narrow) {
+    run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, G::QB>{});
   }
-  run(std::integral_constant<int, G::QB>{});
+  if (Ps) {
+    __syncthreads();  // every wave is done with the ring: reuse it for the sum
+    const double s = block_sum_f64<kWaves>(dsum, reinterpret_cast<double*>(ring));
+    if (tid == 0) partials[blockIdx.x] = s;
+  }
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, int64_t nseq, int S,
-                    float c, hipStream_t stream) {
+                    float c, const DiffOut& diff, hipStream_t stream) {
   const int nqt = (S + Geo<D>::BM - 1) / Geo<D>::BM;
   const int64_t nblocks = nseq * nqt;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const bool fused = diff.prev && nblocks <= diff.capacity;
+  if (diff.nparts) *diff.nparts = fused ? (int)nblocks : 0;
   hipLaunchKernelGGL(spatial_kernel<D>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, S, nqt, (int)nblocks, c);
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, S, nqt, (int)nblocks, c,
+                     fused ? (const bf16*)diff.prev : nullptr, fused ? diff.partials : nullptr);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_spatial_bf16(const void* q, const void* k, const void* v, void* o, int64_t nseq,
-                               int S, int D, float scale, hipStream_t stream) {
+                               int S, int D, float scale, const DiffOut& diff,
+                               hipStream_t stream) {
   const float c = scale * kLog2e;
   switch (D) {
 #define PAB_CASE(d) \
   case d:           \
-    return launch_d<d>(q, k, v, o, nseq, S, c, stream);
+    return launch_d<d>(q, k, v, o, nseq, S, c, diff, stream);
     PAB_CASE(8) PAB_CASE(16) PAB_CASE(24) PAB_CASE(32) PAB_CASE(40) PAB_CASE(48) PAB_CASE(56)
     PAB_CASE(64) PAB_CASE(72) PAB_CASE(80) PAB_CASE(88) PAB_CASE(96) PAB_CASE(104) PAB_CASE(112)
     PAB_CASE(120) PAB_CASE(128)

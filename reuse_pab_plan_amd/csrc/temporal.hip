@@ -71,7 +71,9 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
                                                            const bf16* __restrict__ K,
                                                            const bf16* __restrict__ V,
                                                            bf16* __restrict__ O, int F, int S,
-                                                           int pos_blocks, int nblocks, float c) {
+                                                           int pos_blocks, int nblocks, float c,
+                                                           const bf16* __restrict__ P,
+                                                           double* __restrict__ partials) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) bf16 smem[G::LDS_ELEMS];
   bf16* ks = smem;                     // K runs, frame-major: row f holds positions 0..kPos-1
@@ -148,6 +150,24 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   }
   __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0): this wave's loads have landed
   __syncthreads();
+
+  // Attention difference against a previous output P (when given): the
+  // chunks this thread will store are requested now, so their loads run
+  // under the products; chunk k of the thread is output slot tid + 256 k.
+  constexpr int kOwn = (kMaxF * G::RCH + kThreads - 1) / kThreads;
+  const int valid_out = npos * (D / 8);
+  uint4 prev[kOwn];
+  if (P) {
+    const bf16* pb0 = P + base + (size_t)s0 * D;
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int i = tid + k * kThreads;
+      const int frame = i / G::RCH, ch = i % G::RCH;
+      prev[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (frame < F && ch < valid_out)
+        prev[k] = *reinterpret_cast<const uint4*>(pb0 + (size_t)frame * frame_stride + ch * 8);
+    }
+  }
 
   if (live) {
     const bf16* kp = ks + pos * D;
@@ -264,41 +284,60 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   __syncthreads();
   // O runs back to HBM: run f of the block is contiguous there, written with
   // 16-byte stores in the order of the loads.
-  {
-    const int valid_ch = npos * (D / 8);
-    bf16* ob0 = O + base + (size_t)s0 * D;
-    for (int i = tid; i < F * G::RCH; i += kThreads) {
+  bf16* ob0 = O + base + (size_t)s0 * D;
+  if (P) {
+    double dsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int i = tid + k * kThreads;
       const int frame = i / G::RCH, ch = i % G::RCH;
-      if (ch < valid_ch)
-        *reinterpret_cast<uint4*>(ob0 + (size_t)frame * frame_stride + ch * 8) =
-            *reinterpret_cast<const uint4*>(ks + i * 8);
+      if (frame < F && ch < valid_out) {
+        const uint4 w = *reinterpret_cast<const uint4*>(ks + i * 8);
+        *reinterpret_cast<uint4*>(ob0 + (size_t)frame * frame_stride + ch * 8) = w;
+        dsum += sqdiff_bf16x2(w.x, prev[k].x) + sqdiff_bf16x2(w.y, prev[k].y) +
+                sqdiff_bf16x2(w.z, prev[k].z) + sqdiff_bf16x2(w.w, prev[k].w);
+      }
     }
+    __syncthreads();  // every thread is done with the staged output: reuse LDS for the sum
+    const double s = block_sum_f64<kWaves>(dsum, reinterpret_cast<double*>(smem));
+    if (tid == 0) partials[blockIdx.x] = s;
+    return;
+  }
+  for (int i = tid; i < F * G::RCH; i += kThreads) {
+    const int frame = i / G::RCH, ch = i % G::RCH;
+    if (ch < valid_out)
+      *reinterpret_cast<uint4*>(ob0 + (size_t)frame * frame_stride + ch * 8) =
+          *reinterpret_cast<const uint4*>(ks + i * 8);
   }
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, int64_t nbh, int F, int S,
-                    float c, hipStream_t stream) {
+                    float c, const DiffOut& diff, hipStream_t stream) {
   const int pos_blocks = (S + kPos - 1) / kPos;
   const int64_t nblocks = nbh * pos_blocks;
   // Direct-load offsets are 32-bit: one (b, h) slab must stay below 4 GiB.
   if (nblocks > 0x7fffffff || F > kMaxF || (int64_t)F * S * D * 2 >= ((int64_t)1 << 32))
     return hipErrorInvalidConfiguration;
+  const bool fused = diff.prev && nblocks <= diff.capacity;
+  if (diff.nparts) *diff.nparts = fused ? (int)nblocks : 0;
   hipLaunchKernelGGL(temporal_kernel<D>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, F, S, pos_blocks,
-                     (int)nblocks, c);
+                     (int)nblocks, c, fused ? (const bf16*)diff.prev : nullptr,
+                     fused ? diff.partials : nullptr);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_temporal_bf16(const void* q, const void* k, const void* v, void* o, int64_t nbh,
-                                int F, int S, int D, float scale, hipStream_t stream) {
+                                int F, int S, int D, float scale, const DiffOut& diff,
+                                hipStream_t stream) {
   const float c = scale * kLog2e;
   switch (D) {
 #define PAB_CASE(d) \
   case d:           \
-    return launch_d<d>(q, k, v, o, nbh, F, S, c, stream);
+    return launch_d<d>(q, k, v, o, nbh, F, S, c, diff, stream);
     PAB_CASE(8) PAB_CASE(16) PAB_CASE(24) PAB_CASE(32) PAB_CASE(40) PAB_CASE(48) PAB_CASE(56)
     PAB_CASE(64) PAB_CASE(72) PAB_CASE(80) PAB_CASE(88) PAB_CASE(96) PAB_CASE(104) PAB_CASE(112)
     PAB_CASE(120) PAB_CASE(128)

@@ -6,9 +6,10 @@ reuses the output broadcast from an earlier step.  The harness plans the
 schedule with ``pab_plan_schedule``, allocates the cache slots (two O-sized
 HBM buffers per block and type), and for every step calls
 ``pab_step_dispatch`` once per attention type, bracketed by HIP events on the
-launch stream, followed on recompute steps by the attention-difference MSE
-between the new output and the one it replaces (PAB article, Figure 1
-caption).  torch supplies device memory, streams and events only.
+launch stream; with drift on, the dispatcher also takes the attention
+difference (MSE) between each recompute and the output it replaces (PAB
+article, Figure 1 caption).  torch supplies device memory, streams and
+events only.
 
 ``CONFIGS`` holds the synthetic workloads, stand-ins for the video DiTs the
 pages measure (480p and 720p latent shapes, a 28-block stack, a full-3D
@@ -301,6 +302,14 @@ class Trajectory:
                 self._types.append(t)
             self._descs.append(row)
 
+    def replan(self):
+        """Plan the schedule again (as a trajectory does before its first
+        step) and check it is the one the descriptors were built on."""
+        ranges = list(self.cfg.ranges) if self.pab else [0] * len(self.cfg.kinds)
+        rec, _, _ = lib.pab_plan_schedule(self.cfg.N, ranges)
+        if not np.array_equal(rec, self.recompute):
+            raise RuntimeError("the schedule changed between plans")
+
     def steps_needed(self):
         return [(b, a, i) for b in range(self.cfg.blocks) for a in range(self.T)
                 for i in range(self.cfg.N) if self.recompute[i, a]]
@@ -315,7 +324,6 @@ class Trajectory:
         masks = np.zeros((cfg.blocks, cfg.N), dtype=np.uint32)
         outs = [[[None] * self.T for _ in range(cfg.N)] for _ in range(cfg.blocks)]
         brackets = {"attn": [[] for _ in range(self.T)], "mse": []}
-        last = [[None] * self.T for _ in range(cfg.blocks)]
         mk = (lambda: torch.cuda.Event(enable_timing=True)) if events else None
         text_done = set()  # blocks whose constant text K/V this run has projected
         with torch.cuda.stream(self.stream):
@@ -343,6 +351,10 @@ class Trajectory:
                         elif rec:
                             q, k, v = self.inputs.get(b, a, i)
                             t[0].q, t[0].k, t[0].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+                        # With drift on, the dispatcher itself takes the
+                        # attention difference of each recompute against the
+                        # previous one of its type (into drift_out[b, a, i]).
+                        t[0].drift = self.drift_out[b, a].data_ptr() if self.drift else None
                         if events and rec:
                             e0, e1 = mk(), mk()
                             e0.record(self.stream)
@@ -352,28 +364,9 @@ class Trajectory:
                             brackets["attn"][a].append((e0, e1))
                         masks[b, i] |= mask << a
                         outs[b][i][a] = ptrs[0]
-                        if rec and self.drift and last[b][a] is not None:
-                            if events:
-                                m0, m1 = mk(), mk()
-                                m0.record(self.stream)
-                            self._mse(ptrs[0], last[b][a], self.drift_out[b, a, i])
-                            if events:
-                                m1.record(self.stream)
-                                brackets["mse"].append((m0, m1))
-                        if rec:
-                            last[b][a] = ptrs[0]
                 if on_step is not None:
                     on_step(i, outs)
         return {"masks": masks, "outs": outs, "brackets": brackets}
-
-    def _mse(self, a_ptr, b_ptr, out):
-        n = int(np.prod(self.cfg.video_shape))  # a module output has as many elements
-        st = lib.load().pab_attn_diff_mse(
-            C.c_void_p(a_ptr), C.c_void_p(b_ptr), n,
-            lib.PAB_BF16 if self.cfg.dtype == "bf16" else lib.PAB_F32,
-            C.c_void_p(out.data_ptr()), C.c_void_p(self.ws.data_ptr()), self.ws.numel(),
-            C.c_void_p(self.stream.cuda_stream))
-        lib._check("pab_attn_diff_mse", st)
 
     def slot_tensor(self, b, a, ptr):
         """The cache slot tensor that lives at device address ``ptr``."""

@@ -153,20 +153,46 @@ def test_stack28_cache_first_steps():
     _run_checked(cfg, blocks_checked=(0, 13, 27), check_steps=(5,), resident=False, max_steps=8)
 
 
-def test_drift_matches_oracle_mse():
+# Shapes of the drift test: each reaches a different way the dispatcher takes
+# the difference.  bf16 attention kernels fold it into their output pass
+# (spatial with 64- and 32-row query blocks per wave, temporal with one and two
+# 32-frame blocks, cross with 1, 2 and 4 32-key blocks); a separate pass takes
+# it for cross attention whose previous-output ring does not fit in LDS
+# (D = 128, more than 64 text tokens), padded prompts (one cross launch per
+# batch entry) and fp32.
+DRIFT_CASES = [
+    # B, H, F, S, D, L, text_len, dtype
+    (1, 2, 4, 96, 72, 40, None, "bf16"),
+    (2, 3, 5, 333, 128, 77, None, "bf16"),
+    (1, 1, 33, 45, 8, 1, None, "bf16"),
+    (2, 2, 2, 517, 40, 128, None, "bf16"),
+    (1, 2, 64, 7, 64, 64, None, "bf16"),
+    (2, 2, 3, 130, 72, 120, (120, 33), "bf16"),
+    (1, 2, 3, 70, 24, 20, None, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DRIFT_CASES, ids=lambda c: "x".join(map(str, c[:6])) +
+                         ("-padded" if c[6] else "") + "-" + c[7])
+def test_drift_matches_oracle_mse(case):
     # PAB off: consecutive-step attention differences (the Figure 1 analogue),
     # computed on the device by the dispatcher's own two-slot drift path.
     _need_gpu()
-    cfg = harness.Config("drift", "bf16", 1, 2, 4, 96, 72, 40, 10,
-                         ("spatial", "temporal", "cross"), (0, 0, 0), 1, 12, "drift")
+    B, H, F, S, D, L, text_len, dt = case
+    print(f"[case] drift {case}", flush=True)
+    cfg = harness.Config("drift", dt, B, H, F, S, D, L, 10,
+                         ("spatial", "temporal", "cross"), (0, 0, 0), 1, 12, "drift",
+                         text_len=text_len)
     dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     rec, _, _ = lib.pab_plan_schedule(cfg.N, [0, 0, 0])
     inputs = harness.Inputs(cfg, [(0, a, i) for a in range(3) for i in range(cfg.N)], device=dev)
-    slots = [(torch.empty(cfg.video_shape, dtype=torch.bfloat16, device=dev),
-              torch.empty(cfg.video_shape, dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+    slots = [(torch.empty(cfg.video_shape, dtype=tdt, device=dev),
+              torch.empty(cfg.video_shape, dtype=tdt, device=dev)) for _ in range(3)]
     drift = torch.full((3, cfg.N), -1.0, dtype=torch.float64, device=dev)
     n = int(np.prod(cfg.video_shape))
     ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    lens = None if text_len is None else np.ascontiguousarray(np.asarray(text_len, dtype=np.int32))
     types = (lib.TypeDesc * 3)()
     for a, kind in enumerate(cfg.kinds):
         types[a].kind = lib.KINDS[kind]
@@ -175,10 +201,13 @@ def test_drift_matches_oracle_mse():
         types[a].B, types[a].H, types[a].F, types[a].S, types[a].D = cfg.video_shape
         types[a].L = cfg.L
         types[a].drift = drift[a].data_ptr()
+        if kind == "cross" and lens is not None:
+            types[a].text_len = lens.ctypes.data_as(C.POINTER(C.c_int32))
     stream = torch.cuda.current_stream()
     desc = lib.StepDesc(num_steps=cfg.N, num_types=3,
                         recompute=rec.ctypes.data_as(C.POINTER(C.c_uint8)),
-                        types=C.cast(types, C.POINTER(lib.TypeDesc)), dtype=lib.PAB_BF16,
+                        types=C.cast(types, C.POINTER(lib.TypeDesc)),
+                        dtype=lib.PAB_BF16 if dt == "bf16" else lib.PAB_F32,
                         softmax_scale=0.0, workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
                         stream=stream.cuda_stream)
     prev = [None] * 3
@@ -192,14 +221,14 @@ def test_drift_matches_oracle_mse():
         torch.cuda.synchronize()
         for a in range(3):
             cur = [s for s in slots[a] if s.data_ptr() == outs[a]][0]
-            host = cur.float().cpu().numpy()
+            host = cur.double().cpu().numpy()
             if prev[a] is not None:
                 expect[a, i] = oracle.mse(host, prev[a])
             prev[a] = host
     got = drift.cpu().numpy()
     assert (got[:, 0] == -1.0).all()  # no predecessor: left untouched
     rel = np.abs(got[:, 1:] - expect[:, 1:]) / expect[:, 1:]
-    print(f"[parity] drift max rel err {rel.max():.2e}", flush=True)
+    print(f"[parity] drift {case} max rel err {rel.max():.2e}", flush=True)
     assert rel.max() <= 1e-6
     # The synthetic workload's U shape: outer steps differ more than inner ones.
     assert got[:, 1].min() > 10 * got[:, 4:8].max()
