@@ -307,7 +307,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    brackets = {"attn": [[] for _ in cfg.kinds], "mse": []}
+    brackets = {"attn": [[] for _ in cfg.kinds], "diff": [[] for _ in cfg.kinds]}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -316,6 +316,7 @@ def main():
         r = traj_on.run(events=True)
         for a in range(len(cfg.kinds)):
             brackets["attn"][a] += r["brackets"]["attn"][a]
+            brackets["diff"][a] += r["brackets"]["diff"][a]
     stop.record(stream)
     torch.cuda.synchronize()
     on_ms = start.elapsed_time(stop) / args.steps
@@ -387,12 +388,20 @@ def main():
         peaks = lib.measure_peaks(dev, stream)
         log("measured peaks: " + ", ".join(f"{k} {v:.0f}" for k, v in peaks.items()))
 
+    # Per-type launch statistics over the timed trajectories' recomputes that
+    # have a predecessor: the attention with the difference against that
+    # predecessor folded into its output pass (where the kernel's LDS and the
+    # workspace allow; else a separate pass inside the same bracket) and the
+    # difference's final reduction.  Their algorithmic bytes add one read of
+    # the previous output to the attention's own.
     kernels = {}
     for a, kind in enumerate(cfg.kinds):
-        st = stats_ms(brackets["attn"][a])
+        with_diff = [ev for ev, d in zip(brackets["attn"][a], brackets["diff"][a]) if d]
+        st = stats_ms(with_diff or brackets["attn"][a])
         flops = harness.attn_flops(cfg, kind)
-        by = harness.attn_bytes(cfg, kind)
+        by = harness.attn_bytes(cfg, kind) + (harness.mse_bytes(cfg) // 2 if with_diff else 0)
         st.update({
+            "with_difference": bool(with_diff),
             "launches_per_trajectory": int(traj_on.counts[a]) * cfg.blocks,
             "flops_per_launch": flops,
             "bytes_per_launch": by,

@@ -317,13 +317,16 @@ class Trajectory:
     def run(self, events: bool = False, on_step=None, max_steps=None):
         """Run the trajectory (its first ``max_steps`` steps if given).
         Returns a dict with the dispatch masks, output pointers and (if
-        events) per-type kernel and MSE brackets."""
+        events) per-type dispatch brackets: brackets["attn"][a] holds one event
+        pair per recompute, and brackets["diff"][a] says for each whether it
+        also took the attention difference (drift on, a predecessor exists)."""
         import torch
 
         cfg = self.cfg
         masks = np.zeros((cfg.blocks, cfg.N), dtype=np.uint32)
         outs = [[[None] * self.T for _ in range(cfg.N)] for _ in range(cfg.blocks)]
-        brackets = {"attn": [[] for _ in range(self.T)], "mse": []}
+        brackets = {"attn": [[] for _ in range(self.T)], "diff": [[] for _ in range(self.T)]}
+        done = np.zeros((cfg.blocks, self.T), dtype=bool)  # a recompute happened this run
         mk = (lambda: torch.cuda.Event(enable_timing=True)) if events else None
         text_done = set()  # blocks whose constant text K/V this run has projected
         with torch.cuda.stream(self.stream):
@@ -362,6 +365,9 @@ class Trajectory:
                         if events and rec:
                             e1.record(self.stream)
                             brackets["attn"][a].append((e0, e1))
+                            brackets["diff"][a].append(bool(self.drift and done[b, a]))
+                        if rec:
+                            done[b, a] = True
                         masks[b, i] |= mask << a
                         outs[b][i][a] = ptrs[0]
                 if on_step is not None:
