@@ -215,7 +215,9 @@ int pab_proj_out(const void* o, const void* w, void* y, int32_t B, int32_t F, in
 
 /*
  * pab_mse_workspace_bytes -- device workspace pab_attn_diff_mse needs for
- * n elements (partial sums, one double per reduction block).
+ * n elements (partial sums, one double per reduction block).  The same size
+ * also holds the per-block partials of an attention kernel that takes the
+ * difference in its output pass (pab_step_dispatch, drift).
  */
 size_t pab_mse_workspace_bytes(int64_t n);
 
@@ -292,7 +294,12 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
  *   for each type a: if recompute[step*num_types + a], launch a's kernel
  *   into its next slot (and the drift MSE if requested); otherwise launch
  *   nothing -- the slot last written holds the source step's output bytes,
- *   reused in place (zero copy, bit-exact).
+ *   reused in place (zero copy, bit-exact).  The drift MSE is the same
+ *   quantity pab_attn_diff_mse computes (fp64 differences and sums, a fixed
+ *   order per launch shape): bf16 attention kernels take it in their output
+ *   pass, reading the previous slot beside each store; fp32, padded prompts,
+ *   attention modules and cross attention whose LDS has no room for it take
+ *   a separate pass.
  *   recomputed_mask (may be NULL): bit a set iff type a recomputed.
  *   outputs (may be NULL): host array of num_types pointers, set to the slot
  *   holding this step's output of each type.

@@ -33,6 +33,9 @@
 //     bf16-rounded p that multiply V -- on the MFMA.
 // Blocks are remapped so that the query tiles of one sequence share an XCD
 // (and its L2), where the sequence's K and V stay resident.
+// With a previous output P (the attention difference of PAB's Figure 1), the
+// output pass also reads P beside its stores and each block writes the fp64
+// sum of squared differences of the stored values.
 #include <type_traits>
 
 #include "device.hpp"

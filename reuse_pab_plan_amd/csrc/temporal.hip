@@ -16,7 +16,10 @@
 //     (ds_read_b64_tr_b16) and an all-ones operand row D that yields the
 //     softmax denominator;
 //   * the output is staged frame-major in the K buffer and written back run
-//     by run with lane-contiguous 16-byte stores.
+//     by run with lane-contiguous 16-byte stores; with a previous output P
+//     (the attention difference) the same chunks of P are read into
+//     registers under the products and each block writes the fp64 sum of
+//     squared differences of what it stores.
 #include "device.hpp"
 #include "launch.hpp"
 
