@@ -172,14 +172,45 @@ DRIFT_CASES = [
 ]
 
 
+def _high_word_slots(shape, dev):
+    """Two bf16 slot tensors whose device addresses have bit 31 of the low
+    32-bit word set (views into one pool): kernels that move a base address
+    into scalar registers must not sign-extend that word."""
+    n = int(np.prod(shape))
+    nbytes = 2 * n
+    align = 1 << 12
+    pool = torch.empty((1 << 31) + 2 * nbytes + 2 * align, dtype=torch.uint8, device=dev)
+    base = pool.data_ptr()
+    off = ((1 << 31) - (base & 0xFFFFFFFF)) % (1 << 32)
+    off = (off + align - 1) // align * align
+    views = []
+    for i in range(2):
+        o = off + i * ((nbytes + align - 1) // align * align)
+        t = pool[o:o + nbytes].view(torch.bfloat16).view(shape)
+        assert (t.data_ptr() & 0xFFFFFFFF) >= 1 << 31
+        views.append(t)
+    return pool, views
+
+
 @pytest.mark.parametrize("case", DRIFT_CASES, ids=lambda c: "x".join(map(str, c[:6])) +
                          ("-padded" if c[6] else "") + "-" + c[7])
 def test_drift_matches_oracle_mse(case):
+    _drift_case(case)
+
+
+def test_drift_slots_at_high_addresses():
+    # Regression: cache slots whose addresses have bit 31 of the low word set.
+    # A direct load whose base address was assembled from two readfirstlane
+    # results (which return int) once sign-extended that word and faulted.
+    _drift_case((1, 2, 4, 96, 72, 40, None, "bf16"), high_slots=True)
+
+
+def _drift_case(case, high_slots=False):
     # PAB off: consecutive-step attention differences (the Figure 1 analogue),
     # computed on the device by the dispatcher's own two-slot drift path.
     _need_gpu()
     B, H, F, S, D, L, text_len, dt = case
-    print(f"[case] drift {case}", flush=True)
+    print(f"[case] drift {case} high_slots={high_slots}", flush=True)
     cfg = harness.Config("drift", dt, B, H, F, S, D, L, 10,
                          ("spatial", "temporal", "cross"), (0, 0, 0), 1, 12, "drift",
                          text_len=text_len)
@@ -189,6 +220,10 @@ def test_drift_matches_oracle_mse(case):
     inputs = harness.Inputs(cfg, [(0, a, i) for a in range(3) for i in range(cfg.N)], device=dev)
     slots = [(torch.empty(cfg.video_shape, dtype=tdt, device=dev),
               torch.empty(cfg.video_shape, dtype=tdt, device=dev)) for _ in range(3)]
+    pool = None
+    if high_slots:  # the spatial type's two slots
+        pool, hs = _high_word_slots(cfg.video_shape, dev)
+        slots[0] = (hs[0], hs[1])
     drift = torch.full((3, cfg.N), -1.0, dtype=torch.float64, device=dev)
     n = int(np.prod(cfg.video_shape))
     ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=dev)
