@@ -53,6 +53,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;           // lazy-rescale threshold (log2 units)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // Smallest row stride (elements, multiple of 8, >= min_elems) whose first four
@@ -109,6 +110,7 @@ struct Geo {
   static_assert((kBN - 1) * VS + (LAST_READ ? NB : NB - 1) * 32 <= VREG + VSLACK,
                 "V over-read must stay in the stage");
   static_assert(NST * STAGE * 2 <= kLds, "LDS ring too large");
+  static_assert(2 * 32 * QB * D * 2 <= STAGE * 2, "two waves' output rows fit one stage");
   static_assert((NST - 2) * NJW < 64, "vmcnt budget");
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
@@ -222,6 +224,34 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
   // Barrier B_t: tile t has landed and is visible to every wave; the stage
   // read last by unit 2t-3 is free again and is refilled with the tile
   // NST-2 ahead.
+  // The previous output P (attention difference) with a four-stage ring:
+  // once the last tile is synchronized, stages nt and nt+1 (mod 4) are
+  // never refilled and every wave is done reading them (the scores taken
+  // after the last unit read stage nt, but are discarded), so each wave
+  // brings its own rows of P into half of one of them by direct loads,
+  // under the last tile's work.  A wave reads back only what it loaded.
+  int prow0 = 0, prows = 0;  // this wave's query rows (set by run)
+  auto prev_lds = [&]() -> uint32_t {
+    return stage_base(nt + (wave >> 1)) + (uint32_t)((wave & 1) * prows * D * 2);
+  };
+  auto issue_prev = [&]() {
+    if (prow0 >= S) return;
+    const uint32_t bytes = (uint32_t)(prows * D * 2);
+    const uint32_t valid = (uint32_t)(min(prows, S - prow0) * D * 2);
+    // The base goes to scalar registers; each half is taken as an unsigned
+    // 32-bit value (readfirstlane returns int: widening it directly would
+    // sign-extend the low half).
+    const uint64_t pa = (uint64_t)(uintptr_t)(Ps + (size_t)prow0 * D);
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pa);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+    const bf16* pb = (const bf16*)(uintptr_t)(((uint64_t)phi << 32) | (uint64_t)plo);
+    const uint32_t dst = prev_lds();
+    for (uint32_t j = 0; j * 1024 < bytes; ++j) {
+      const uint32_t pos = j * 1024 + (uint32_t)lane * 16;
+      // Rows past S re-read the last valid 16 bytes; lanes past the rows idle.
+      if (pos < bytes) dma16(pb, min(pos, valid - 16u), dst + j * 1024);
+    }
+  };
   auto sync_tile = [&](int t) {
     if (G::NST == 4 && t + 1 < nt) {  // tile t+1 may still be in flight
       if (nj_wave == G::NJW) {
@@ -242,6 +272,8 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
     // This wave's query rows as the B operand (Q^T), resident in registers.
     const int qrow0 = qt * G::BM + wave * 32 * QBX;
     const bool wave_live = qrow0 < S;
+    prow0 = qrow0;
+    prows = 32 * QBX;
     bf16x8 qreg[QBX][G::ND];
 #pragma unroll
     for (int qb = 0; qb < QBX; ++qb) {
@@ -422,13 +454,25 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
     // unit of the last tile when S % 64 is 1..32) has all p exactly 0 and
     // changes nothing; the QK after the last unit runs on stale but in-bounds
     // LDS and is dropped.
+    // The previous output (attention difference) is fetched once the last
+    // tile is synchronized: here, in the last one or two tiles, so the hot
+    // loop above carries none of it.
+    const int t_tail = t;
     for (; t < nt; ++t) {
+      if constexpr (G::NST == 4) {
+        if (Ps && t == nt - 1 && t == t_tail) issue_prev();  // synchronized before the tail
+      }
       const uint32_t cur = stage_base(t);
       const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
       rescale(mA);
       unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB, mB);
       rescale(mB);
-      if (t + 1 < nt) sync_tile(t + 1);
+      if (t + 1 < nt) {
+        sync_tile(t + 1);
+        if constexpr (G::NST == 4) {
+          if (Ps && t + 1 == nt - 1) issue_prev();
+        }
+      }
       const uint32_t kn = opaque(stage_base(t + 1) + klane);
       unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA, mA);
     }
@@ -445,10 +489,14 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
       inv[qb] = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
     }
     if (Ps) {
-      // Attention difference against the previous output: every word of it
-      // is requested before the first is used, so the block waits for one
-      // load latency rather than one per word.
+      // Attention difference against the previous output: from LDS where the
+      // ring brought it in, else from HBM with every word requested before
+      // the first is used (one load latency per block, not one per word).
       uint2 pw[QBX][G::NB][4];
+      if constexpr (G::NST == 4) {
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+      }
 #pragma unroll
       for (int qb = 0; qb < QBX; ++qb) {
         const int qrow = qrow0 + qb * 32 + l32;
@@ -458,8 +506,15 @@ __global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __rest
           for (int g = 0; g < 4; ++g) {
             const int d0 = nb * 32 + g * 8 + h * 4;
             pw[qb][nb][g] = make_uint2(0u, 0u);
-            if (d0 < D && qrow < S)
-              pw[qb][nb][g] = *reinterpret_cast<const uint2*>(Ps + (size_t)qrow * D + d0);
+            if (d0 < D && qrow < S) {
+              if constexpr (G::NST == 4) {
+                const u32x2 t2 =
+                    *LDS_PTR(const u32x2, prev_lds() + (uint32_t)(((qb * 32 + l32) * D + d0) * 2));
+                pw[qb][nb][g] = make_uint2(t2.x, t2.y);
+              } else {
+                pw[qb][nb][g] = *reinterpret_cast<const uint2*>(Ps + (size_t)qrow * D + d0);
+              }
+            }
           }
       }
 #pragma unroll

@@ -179,13 +179,24 @@ def _high_word_slots(shape, dev):
     n = int(np.prod(shape))
     nbytes = 2 * n
     align = 1 << 12
-    pool = torch.empty((1 << 31) + 2 * nbytes + 2 * align, dtype=torch.uint8, device=dev)
+    step = (nbytes + align - 1) // align * align
+    total = 2 * step
+    pool = torch.empty((1 << 31) + 2 * total + align, dtype=torch.uint8, device=dev)
     base = pool.data_ptr()
-    off = ((1 << 31) - (base & 0xFFFFFFFF)) % (1 << 32)
+    # First offset (4 KiB aligned) from which both slots lie where the low
+    # word is in [2^31, 2^32).
+    low = base & 0xFFFFFFFF
+    if low >= 1 << 31 and low + total < 1 << 32:
+        off = 0
+    elif low < 1 << 31:
+        off = (1 << 31) - low
+    else:
+        off = (1 << 32) - low + (1 << 31)
     off = (off + align - 1) // align * align
+    assert off + total <= pool.numel()
     views = []
     for i in range(2):
-        o = off + i * ((nbytes + align - 1) // align * align)
+        o = off + i * step
         t = pool[o:o + nbytes].view(torch.bfloat16).view(shape)
         assert (t.data_ptr() & 0xFFFFFFFF) >= 1 << 31
         views.append(t)
