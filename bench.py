@@ -6,12 +6,12 @@ block (48 frames x 1590 tokens, 16 heads x 72, 120 text tokens, 30 steps,
 broadcast ranges spatial 2 / temporal 4 / cross 6, bf16): the schedule from
 pab_plan_schedule, then per step pab_step_dispatch for each attention type
 (spatial, temporal and cross kernels on recompute steps, nothing on
-broadcast steps).  All inputs of the trajectory are generated into HBM
-before timing starts.  The attention-difference MSE between consecutive
-computations of each type (the quantity the pages plot to motivate the
-broadcast ranges, used to calibrate them) is not part of a production
-trajectory; it is timed in a separate pass over the same trajectory, and its
-per-launch figures are reported with the other kernels.
+broadcast steps), each recompute also taking the attention-difference MSE
+against the previous computation of its type (the quantity the pages plot to
+motivate the broadcast ranges, used to calibrate them; the dispatcher folds
+it into the attention kernels' output pass).  All inputs of the trajectory
+are generated into HBM before timing starts.  The same trajectory without
+the difference, as a production run would take it, is reported beside it.
 
 Prints one JSON line: metric, value (attention TFLOP/s executed per second
 of PAB-on trajectory), ms_per_step (ms per PAB-on trajectory), the PAB-off
@@ -19,7 +19,8 @@ trajectory beside it, per-kernel timings, the roofline of the dominant
 kernel (spatial attention, bf16 MFMA) measured live with HIP events on the
 launch stream, and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--config b480|b720|full3d|tiny]
+    python bench.py [--steps K] [--warmup W] [--config b480|b720|full3d|cfg480|stack28|tiny]
+                    [--module-config b480m|""] [--stream-inputs] [--no-peaks]
                     [--no-cpu-baseline] [--calib-copy]
 """
 
