@@ -114,3 +114,67 @@ def test_fullsize_mse(name):
     ref = oracle.mse(x.float().cpu().numpy(), y.float().cpu().numpy())
     print(f"[parity] {name} mse rel err {abs(got - ref) / ref:.2e}", flush=True)
     assert abs(got - ref) <= 1e-6 * ref
+
+
+@pytest.mark.parametrize("name", ["b480", "b720", "full3d"])
+def test_fullsize_dispatch_drift(name):
+    # The attention difference as the benchmark step takes it: through
+    # pab_step_dispatch with drift on, folded into the attention kernels'
+    # output pass at the workload's full shape.  Two consecutive recomputes
+    # of every type (steps w0 and w0 + 1); the drift of the second must be
+    # the fp64 MSE of the two stored outputs over the whole tensor, and each
+    # output must equal the plain kernel's, bit for bit.
+    import ctypes as C
+
+    _need_gpu()
+    cfg = harness.CONFIGS[name]
+    T = len(cfg.kinds)
+    w0 = -(-15 * cfg.N // 100)
+    rec, _, _ = lib.pab_plan_schedule(cfg.N, [0] * T)
+    n = int(np.prod(cfg.video_shape))
+    slots = [(torch.empty(cfg.video_shape, dtype=torch.bfloat16, device="cuda:0"),
+              torch.empty(cfg.video_shape, dtype=torch.bfloat16, device="cuda:0")) for _ in range(T)]
+    drift = torch.full((T, cfg.N), -1.0, dtype=torch.float64, device="cuda:0")
+    ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device="cuda:0")
+    types = (lib.TypeDesc * T)()
+    for a, kind in enumerate(cfg.kinds):
+        types[a].kind = lib.KINDS[kind]
+        types[a].slot[0] = slots[a][0].data_ptr()
+        types[a].slot[1] = slots[a][1].data_ptr()
+        types[a].B, types[a].H, types[a].F, types[a].S, types[a].D = cfg.video_shape
+        types[a].L = cfg.L
+        types[a].drift = drift[a].data_ptr()
+    desc = lib.StepDesc(num_steps=cfg.N, num_types=T,
+                        recompute=rec.ctypes.data_as(C.POINTER(C.c_uint8)),
+                        types=C.cast(types, C.POINTER(lib.TypeDesc)), dtype=lib.PAB_BF16,
+                        softmax_scale=0.0, workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
+                        stream=torch.cuda.current_stream().cuda_stream)
+    # The dispatcher reads slot parity off the schedule, so the steps before
+    # w0 need not run (the drift at w0 then compares against a slot no step
+    # wrote and is not checked).
+    outs = {}
+    for i in range(w0, w0 + 2):
+        inputs = [_gen(cfg, a, i) for a in range(T)]
+        for a in range(T):
+            q, k, v = inputs[a]
+            types[a].q, types[a].k, types[a].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+        mask, ptrs = lib.pab_step_dispatch(desc, i)
+        assert mask == (1 << T) - 1
+        if i >= w0:
+            torch.cuda.synchronize()
+            for a, kind in enumerate(cfg.kinds):
+                cur = [s for s in slots[a] if s.data_ptr() == ptrs[a]][0]
+                outs[(a, i)] = cur.clone()
+                q, k, v = inputs[a]
+                plain = torch.empty_like(q)
+                {"spatial": lib.pab_attn_spatial, "temporal": lib.pab_attn_temporal,
+                 "cross": lib.pab_attn_cross}[kind](q, k, v, plain)
+                torch.cuda.synchronize()
+                assert torch.equal(cur, plain), (name, kind, i)
+        del inputs
+    got = drift.cpu().numpy()
+    for a, kind in enumerate(cfg.kinds):
+        ref = oracle.mse(_host(outs[(a, w0 + 1)]), _host(outs[(a, w0)]))
+        rel = abs(got[a, w0 + 1] - ref) / ref
+        print(f"[parity] {name} {kind} dispatch drift rel err {rel:.2e}", flush=True)
+        assert rel <= 1e-6, (name, kind, got[a, w0 + 1], ref)
