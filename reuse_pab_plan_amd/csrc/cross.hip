@@ -23,7 +23,9 @@
 //     the current one computes; the tile's output is staged row-major in the
 //     same stage and written with lane-contiguous 16-byte stores.
 //   * With a previous output to compare against (the attention difference),
-//     its tile comes in beside the query tile, into a second ring, and the
+//     its tile comes into the query tile's own stage once Q is in registers
+//     (direct loads again, under the scores and PV); each lane takes its
+//     chunks into registers before the output is staged there, and the
 //     copy-out accumulates the squared differences.
 #include "device.hpp"
 #include "launch.hpp"
@@ -110,7 +112,7 @@ struct Geo {
 };
 
 template <int D, int NKB, bool DIFF>
-__global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restrict__ Q,
                                                            const bf16* __restrict__ Kt,
                                                            const bf16* __restrict__ Vt,
                                                            bf16* __restrict__ O, int64_t nq, int L, int Lrows,
@@ -119,15 +121,12 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
                                                            const bf16* __restrict__ P,
                                                            double* __restrict__ partials) {
   using G = Geo<D, NKB>;
-  // Direct loads per query tile: the tile, and the previous output's tile.
-  constexpr int QJ = DIFF ? 2 * G::NQJ : G::NQJ;
+  constexpr int QJ = G::NQJ;  // direct loads per query tile
   __shared__ __attribute__((aligned(16))) bf16 ks[G::KROWS * G::KS];
   __shared__ __attribute__((aligned(16))) bf16 vs[G::VROWS * G::VS + G::VSLACK];
   // Per-wave two-stage ring of query tiles (each stage later holds the
   // tile's output, row-major).
   __shared__ __attribute__((aligned(16))) bf16 qstage[kWaves][2][G::QSTAGE];
-  // Previous output tiles (attention difference only).
-  __shared__ __attribute__((aligned(16))) bf16 pstage[DIFF ? kWaves : 1][2][DIFF ? G::QSTAGE : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -210,10 +209,10 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
   // load j copies tile bytes [1024 j + 16 l, +16), clamped to the tile's last
   // valid 16 bytes (rows past nq re-read it: finite values whose outputs are
   // not stored).
-  auto issue_q = [&](int tile, uint32_t st, uint32_t pst) {
+  auto issue_tile = [&](const bf16* base, int tile, uint32_t st) {
     const int64_t rows_left = nq - (int64_t)tile * 32;
     const uint32_t valid = (uint32_t)((rows_left >= 32 ? 32 : rows_left) * D * 2);
-    const bf16* tb = Qh + (int64_t)tile * 32 * D;
+    const bf16* tb = base + (int64_t)tile * 32 * D;
 #pragma unroll
     for (int j = 0; j < G::NQJ; ++j) {
       const uint32_t pos = (uint32_t)(j * 1024 + lane * 16);
@@ -221,20 +220,11 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
       // Lanes past the stage stay idle (their LDS bytes are not written).
       if (j + 1 < G::NQJ || pos < (uint32_t)(32 * D * 2)) dma16(tb, off, st + (uint32_t)(j * 1024));
     }
-    if (DIFF) {
-      const bf16* pb = Ph + (int64_t)tile * 32 * D;
-#pragma unroll
-      for (int j = 0; j < G::NQJ; ++j) {
-        const uint32_t pos = (uint32_t)(j * 1024 + lane * 16);
-        const uint32_t off = min(pos, valid - 16u);
-        if (j + 1 < G::NQJ || pos < (uint32_t)(32 * D * 2)) dma16(pb, off, pst + (uint32_t)(j * 1024));
-      }
-    }
   };
 
   // One 32-row query tile against the text keys: full-row softmax,
   // O = P V / sum(P) on the MFMA, row-major staging, coalesced stores.
-  auto compute = [&](bf16* ost, const bf16* pst, int tile) {
+  auto compute = [&](bf16* ost, int tile) {
     // Q^T operand: lane (row l32, half h) holds d = ds*16 + h*8 .. +7.
     const uint32_t qlane = (uint32_t)(uintptr_t)LDS_PTR(void, ost) + (uint32_t)((l32 * D + h * 8) * 2);
     u32x4 q[G::ND];
@@ -247,6 +237,12 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
         const u32x4 lo = *LDS_PTR(const u32x4, qlane + (uint32_t)(ds * 32) - (uint32_t)(h * 16));
         q[ds] = h == 0 ? lo : pad;
       }
+    }
+    if constexpr (DIFF) {
+      // The stage is free once Q is in registers: the previous output's tile
+      // comes into it by direct loads while the scores and PV run.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the Q reads are done
+      issue_tile(Ph, tile, (uint32_t)(uintptr_t)LDS_PTR(void, ost));
     }
     f32x16 sacc[NKB];
 #pragma unroll
@@ -301,6 +297,25 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
       }
     }
 
+    // The previous output's chunks this lane will store, into registers before
+    // the output overwrites the stage (a wave's LDS operations run in order).
+    constexpr int kOutChunks = 32 * D / 8;
+    const int64_t rows_left = nq - (int64_t)tile * 32;
+    const int valid_chunks = rows_left >= 32 ? kOutChunks : (int)rows_left * (D / 8);
+    uint4 pv[DIFF ? G::NOST : 1];
+    if constexpr (DIFF) {
+      wait_vmcnt<0>();  // the previous output's tile has landed
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < G::NOST; ++i) {
+        const int ch = i * kWave + lane;
+        pv[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (ch < valid_chunks) {
+          const u32x4 t4 = *LDS_PTR(const u32x4, (uint32_t)(uintptr_t)LDS_PTR(void, ost) + (uint32_t)(ch * 16));
+          pv[i] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+        }
+      }
+    }
     const HalfPair pr = half_pair(oacc[G::NBD][G::RD]);
     const float inv = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
     // Accumulators -> row-major tile in LDS (lane: row l32, 4 d per piece).
@@ -317,9 +332,6 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
       }
     __builtin_amdgcn_wave_barrier();
     // Tile rows are contiguous in HBM: copy out 1 KB per instruction.
-    constexpr int kOutChunks = 32 * D / 8;
-    const int64_t rows_left = nq - (int64_t)tile * 32;
-    const int valid_chunks = rows_left >= 32 ? kOutChunks : (int)rows_left * (D / 8);
     bf16* obase = Oh + (int64_t)tile * 32 * D;
 #pragma unroll
     for (int i = 0; i < (kOutChunks + kWave - 1) / kWave; ++i) {
@@ -327,8 +339,8 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
       if (ch < valid_chunks) {
         const uint4 w = *reinterpret_cast<const uint4*>(&ost[ch * 8]);
         *reinterpret_cast<uint4*>(obase + ch * 8) = w;
-        if (DIFF) {
-          const uint4 pw = *reinterpret_cast<const uint4*>(&pst[ch * 8]);
+        if constexpr (DIFF) {
+          const uint4 pw = pv[i];
           dsum += sqdiff_bf16x2(w.x, pw.x) + sqdiff_bf16x2(w.y, pw.y) + sqdiff_bf16x2(w.z, pw.z) +
                   sqdiff_bf16x2(w.w, pw.w);
         }
@@ -343,21 +355,19 @@ __global__ __launch_bounds__(kThreads, DIFF ? 1 : 2) void cross_kernel(const bf1
   // (NOST instructions, always a full tile) and the loads of tile k+1 (QJ).
   const uint32_t st0 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][0]);
   const uint32_t st1 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][1]);
-  const uint32_t ps0 = DIFF ? (uint32_t)(uintptr_t)LDS_PTR(void, pstage[DIFF ? wave : 0][0]) : 0u;
-  const uint32_t ps1 = DIFF ? (uint32_t)(uintptr_t)LDS_PTR(void, pstage[DIFF ? wave : 0][1]) : 0u;
   const int first = t_begin + wave;
   const int n = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
-  if (n > 0) issue_q(first, st0, ps0);
+  if (n > 0) issue_tile(Qh, first, st0);
   for (int k = 0; k < n; ++k) {
     const int tile = first + k * kWaves;
     const bool more = k + 1 < n;
-    if (more) issue_q(tile + kWaves, (k & 1) ? st0 : st1, (k & 1) ? ps0 : ps1);
+    if (more) issue_tile(Qh, tile + kWaves, (k & 1) ? st0 : st1);
     if (k >= 1) {
       if (more) wait_vmcnt<G::NOST + QJ>(); else wait_vmcnt<G::NOST>();
     } else {
       if (more) wait_vmcnt<QJ>(); else wait_vmcnt<0>();
     }
-    compute(qstage[wave][k & 1], DIFF ? pstage[DIFF ? wave : 0][k & 1] : nullptr, tile);
+    compute(qstage[wave][k & 1], tile);
   }
   if (DIFF) {
     __syncthreads();  // every wave is done with its ring: reuse it for the sum
@@ -376,13 +386,7 @@ hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int
   // most 96 query tiles per block (the text K/V load is amortized over them).
   using G = Geo<D, NKB>;
   constexpr int kLdsBytes = (G::KROWS * G::KS + G::VROWS * G::VS + G::VSLACK) * 2 +
-                            (DIFF ? 2 : 1) * kWaves * 2 * G::QSTAGE * 2;
-  if constexpr (DIFF && kLdsBytes > 160 * 1024) {
-    // No room for the previous output's ring (wide heads with many text
-    // tokens): plain launch, nparts stays 0 and the caller takes the
-    // difference in a separate pass.
-    return launch_dk<D, NKB, false>(q, kt, vt, o, nbh, nq, L, Lrows, c, diff, stream);
-  } else {
+                            kWaves * 2 * G::QSTAGE * 2;
   constexpr int kPerCu = (160 * 1024) / kLdsBytes >= 2 ? 2 : 1;
   const int64_t ntiles = (nq + 31) / 32;
   const int64_t wave_blocks = 256 * kPerCu;
@@ -407,7 +411,6 @@ hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int
                      Lrows, (int)tiles_per_block, (int)blocks_per_bh, (int)nblocks, c,
                      DIFF ? (const bf16*)diff.prev : nullptr, DIFF ? diff.partials : nullptr);
   return hipGetLastError();
-  }
 }
 
 template <int D, bool DIFF>
@@ -420,7 +423,8 @@ hipError_t launch_dd(const void* q, const void* kt, const void* vt, void* o, int
 }
 
 // The fused difference needs one partial per block: at most the blocks of
-// the grid, which launch_dk sizes to at most ntiles per (b, h).
+// the grid, which launch_dk sizes to at most ntiles per (b, h); it takes no
+// LDS beyond the plain kernel's.
 template <int D>
 hipError_t launch_d(const void* q, const void* kt, const void* vt, void* o, int64_t nbh, int64_t nq,
                     int L, int Lrows, float c, const DiffOut& diff, hipStream_t stream) {

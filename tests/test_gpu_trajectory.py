@@ -155,11 +155,10 @@ def test_stack28_cache_first_steps():
 
 # Shapes of the drift test: each reaches a different way the dispatcher takes
 # the difference.  bf16 attention kernels fold it into their output pass
-# (spatial with 64- and 32-row query blocks per wave, temporal with one and two
-# 32-frame blocks, cross with 1, 2 and 4 32-key blocks); a separate pass takes
-# it for cross attention whose previous-output ring does not fit in LDS
-# (D = 128, more than 64 text tokens), padded prompts (one cross launch per
-# batch entry) and fp32.
+# (spatial with 64- and 32-row query blocks per wave and with three- and
+# four-stage rings, temporal with one and two 32-frame blocks, cross with 1, 2
+# and 4 32-key blocks, up to D = 128); a separate pass takes it for padded
+# prompts (one cross launch per batch entry) and fp32.
 DRIFT_CASES = [
     # B, H, F, S, D, L, text_len, dtype
     (1, 2, 4, 96, 72, 40, None, "bf16"),
