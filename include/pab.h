@@ -297,8 +297,8 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
  *   reused in place (zero copy, bit-exact).  The drift MSE is the same
  *   quantity pab_attn_diff_mse computes (fp64 differences and sums, a fixed
  *   order per launch shape): bf16 attention kernels take it in their output
- *   pass, reading the previous slot beside each store; fp32, padded prompts
- *   and attention modules take a separate pass.
+ *   pass, reading the previous slot beside each store; fp32 and attention
+ *   modules take a separate pass.
  *   recomputed_mask (may be NULL): bit a set iff type a recomputed.
  *   outputs (may be NULL): host array of num_types pointers, set to the slot
  *   holding this step's output of each type.

@@ -194,8 +194,14 @@ int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B,
     for (int32_t b = 0; b < B; ++b) full = full && text_len[b] == L;
   const size_t es = dtype_size(dtype);
   // All text tokens real: one launch.  Otherwise one launch per batch entry,
-  // each over that entry's real tokens (rows stay L apart in memory).
+  // each over that entry's real tokens (rows stay L apart in memory).  With a
+  // fused difference each launch writes its partials after the previous
+  // one's; if one of them cannot (workspace), none counts and the caller
+  // takes the difference in a separate pass.
   const int32_t parts = full ? 1 : B;
+  const bool fuse = diff && diff->prev && diff->nparts && dtype == PAB_BF16;
+  int64_t total_parts = 0;
+  bool all_fused = true;
   for (int32_t b = 0; b < parts; ++b) {
     const int64_t nbh = full ? (int64_t)B * H : H;
     const int32_t len = full ? L : text_len[b];
@@ -207,8 +213,19 @@ int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B,
     char* ob = (char*)o + qo;
     hipError_t e;
     if (dtype == PAB_BF16) {
-      e = launch_cross_bf16(qb, kb, vb, ob, nbh, Nq, len, L, D, c,
-                            (full && diff) ? *diff : DiffOut{}, (hipStream_t)stream);
+      DiffOut db;
+      int np = 0;
+      if (fuse) {
+        db.prev = (const char*)diff->prev + qo;
+        db.partials = diff->partials + total_parts;
+        db.capacity = diff->capacity - total_parts;
+        db.nparts = &np;
+      }
+      e = launch_cross_bf16(qb, kb, vb, ob, nbh, Nq, len, L, D, c, db, (hipStream_t)stream);
+      if (fuse) {
+        all_fused = all_fused && np > 0;
+        total_parts += np;
+      }
     } else {
       SeqLayout lay{nbh, 1, Nq * D, 0, D, (int64_t)L * D, 0, D, Nq, len};
       e = launch_attn_f32((const float*)qb, (const float*)kb, (const float*)vb, (float*)ob, lay, D,
@@ -216,6 +233,7 @@ int run_cross(const void* q, const void* kt, const void* vt, void* o, int32_t B,
     }
     if (e != hipSuccess) return device_error("pab_attn_cross launch", e);
   }
+  if (fuse && all_fused) *diff->nparts = (int)total_parts;
   return ok();
 }
 

@@ -35,8 +35,8 @@ int check_mse(const void* a, const void* b, int64_t n, int32_t dtype, const doub
 // Launch without re-validating (arguments already checked).
 // diff (optional, bf16 only): fuse the attention difference against
 // diff->prev into the output pass when the workspace holds a partial per
-// block (see DiffOut); cross attention fuses it only when every text token is
-// real (one launch).
+// block (see DiffOut); with padded prompts cross attention launches once per
+// batch entry and the partials of the launches follow one another.
 int run_spatial(const void* q, const void* k, const void* v, void* o, int32_t B, int32_t H,
                 int32_t F, int32_t S, int32_t D, int32_t dtype, float scale, void* stream,
                 const DiffOut* diff = nullptr);

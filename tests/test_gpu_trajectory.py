@@ -157,8 +157,9 @@ def test_stack28_cache_first_steps():
 # the difference.  bf16 attention kernels fold it into their output pass
 # (spatial with 64- and 32-row query blocks per wave and with three- and
 # four-stage rings, temporal with one and two 32-frame blocks, cross with 1, 2
-# and 4 32-key blocks, up to D = 128); a separate pass takes it for padded
-# prompts (one cross launch per batch entry) and fp32.
+# and 4 32-key blocks, up to D = 128, and padded prompts, one cross launch per
+# batch entry with their partials one after another); a separate pass takes
+# it for fp32.
 DRIFT_CASES = [
     # B, H, F, S, D, L, text_len, dtype
     (1, 2, 4, 96, 72, 40, None, "bf16"),
