@@ -45,6 +45,9 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS addresses are 32-bit on the device; the host pass (64-bit pointers)
+    # would warn on every cast of one to an LDS pointer it never compiles.
+    "-Xarch_host", "-Wno-int-to-pointer-cast",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -70,12 +70,19 @@ constexpr int odd_chunk_stride(int min_elems) {
 // `gbase` and `lds` must be wave-uniform.  Issued from inline assembly so that
 // its wait (s_waitcnt vmcnt) is placed by hand; the instruction has no
 // result register.
+// m0 is listed as clobbered, which the compiler reports as a reserved
+// register; these kernels never use m0 themselves (their code outside
+// this statement does not touch it), so the clobber only keeps the
+// compiler from relying on m0 across the load.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -106,13 +113,16 @@ struct Geo {
   static constexpr int QSTAGE = 32 * D;                // elements; the last load is partial
   static constexpr int NOST = (32 * D / 8 + kWave - 1) / kWave;  // output stores per tile
   static constexpr bool LAST_READ = (NB - 1) * 32 < D;
+  // LDS of a block: text K and V, and each wave's two-stage query ring.
+  static constexpr int LDS_BYTES = (KROWS * KS + VROWS * VS + VSLACK) * 2 + kWaves * 2 * QSTAGE * 2;
+  static constexpr int PER_CU = (160 * 1024) / LDS_BYTES >= 2 ? 2 : 1;  // resident blocks
   static constexpr int NBD = D / 32;
   static constexpr int HD = ((D % 32) % 8) / 4;
   static constexpr int RD = ((D % 32) / 8) * 4 + (D % 4);
 };
 
 template <int D, int NKB, bool DIFF>
-__global__ __launch_bounds__(kThreads, 2) void cross_kernel(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(kThreads, (Geo<D, NKB>::PER_CU)) void cross_kernel(const bf16* __restrict__ Q,
                                                            const bf16* __restrict__ Kt,
                                                            const bf16* __restrict__ Vt,
                                                            bf16* __restrict__ O, int64_t nq, int L, int Lrows,
@@ -385,9 +395,7 @@ hipError_t launch_dk(const void* q, const void* kt, const void* vt, void* o, int
   // blocks, as many as keep the grid within the fewest waves that leave at
   // most 96 query tiles per block (the text K/V load is amortized over them).
   using G = Geo<D, NKB>;
-  constexpr int kLdsBytes = (G::KROWS * G::KS + G::VROWS * G::VS + G::VSLACK) * 2 +
-                            kWaves * 2 * G::QSTAGE * 2;
-  constexpr int kPerCu = (160 * 1024) / kLdsBytes >= 2 ? 2 : 1;
+  constexpr int kPerCu = G::PER_CU;
   const int64_t ntiles = (nq + 31) / 32;
   const int64_t wave_blocks = 256 * kPerCu;
   int64_t blocks_per_bh = 1;

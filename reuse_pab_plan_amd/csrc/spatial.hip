@@ -110,6 +110,7 @@ struct Geo {
   static_assert((kBN - 1) * VS + (LAST_READ ? NB : NB - 1) * 32 <= VREG + VSLACK,
                 "V over-read must stay in the stage");
   static_assert(NST * STAGE * 2 <= kLds, "LDS ring too large");
+  static constexpr int PER_CU = 2 * NST * STAGE * 2 <= kLds ? 2 : 1;  // resident blocks
   static_assert(2 * 32 * QB * D * 2 <= STAGE * 2, "two waves' output rows fit one stage");
   static_assert((NST - 2) * NJW < 64, "vmcnt budget");
   static constexpr int NBD = D / 32;
@@ -123,12 +124,19 @@ struct Geo {
 // the wait for it (s_waitcnt vmcnt) is placed by hand: the compiler would
 // otherwise wait for every outstanding direct load before each LDS read,
 // serializing the ring.  The instruction has no result register.
+// m0 is listed as clobbered, which the compiler reports as a reserved
+// register; these kernels never use m0 themselves (their code outside
+// this statement does not touch it), so the clobber only keeps the
+// compiler from relying on m0 across the load.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Keeps the compiler from hoisting address arithmetic on `x` out of a loop
 // (it would otherwise spend one VGPR and two adds per distinct LDS offset).
@@ -145,7 +153,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void spatial_kernel(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const bf16* __restrict__ Q,
                                                              const bf16* __restrict__ K,
                                                              const bf16* __restrict__ V,
                                                              bf16* __restrict__ O, int S, int nqt,

@@ -53,12 +53,19 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // global bytes [gbase + voff, +16) and writes LDS bytes [lds + 16*l, +16).
 // `gbase` and `lds` must be wave-uniform.  Inline assembly, so that the wait
 // for it is placed by hand (the compiler does not track these loads).
+// m0 is listed as clobbered, which the compiler reports as a reserved
+// register; these kernels never use m0 themselves (their code outside
+// this statement does not touch it), so the clobber only keeps the
+// compiler from relying on m0 across the load.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // A wave-uniform pointer, moved to scalar registers (the direct load takes
 // its base address from an SGPR pair).
