@@ -159,7 +159,8 @@ def test_stack28_cache_first_steps():
 # four-stage rings, temporal with one and two 32-frame blocks, cross with 1, 2
 # and 4 32-key blocks, up to D = 128, and padded prompts, one cross launch per
 # batch entry with their partials one after another); a separate pass takes
-# it for fp32.
+# it for fp32 and for launches with more blocks than the workspace has
+# partials.
 DRIFT_CASES = [
     # B, H, F, S, D, L, text_len, dtype
     (1, 2, 4, 96, 72, 40, None, "bf16"),
@@ -169,6 +170,10 @@ DRIFT_CASES = [
     (1, 2, 64, 7, 64, 64, None, "bf16"),
     (2, 2, 3, 130, 72, 120, (120, 33), "bf16"),
     (1, 2, 3, 70, 24, 20, None, "f32"),
+    # Many tiny sequences: the workspace holds fewer partials than spatial
+    # (1024) and cross (128) launch blocks, so those two take the separate
+    # pass while temporal (16 blocks) still folds it in.
+    (1, 16, 64, 4, 8, 16, None, "bf16"),
 ]
 
 
