@@ -264,10 +264,15 @@ __global__ __launch_bounds__(kThreads, (Geo<D, NKB>::PER_CU)) void cross_kernel(
         sacc[kb] = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, q[ds]), sacc[kb]);
       }
     }
-    if (!G::BIAS && (L & 31)) {  // ragged key end without a bias column
+    if (!G::BIAS) {  // no bias column: keys from L on are masked in every block that has them
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if ((NKB - 1) * 32 + acc_row(r, h) >= L) sacc[NKB - 1][r] = -INFINITY;
+      for (int kb = 0; kb < NKB; ++kb) {
+        if ((kb + 1) * 32 > L) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + acc_row(r, h) >= L) sacc[kb][r] = -INFINITY;
+        }
+      }
     }
     float mx = sacc[0][0];
 #pragma unroll

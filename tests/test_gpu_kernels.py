@@ -128,6 +128,15 @@ CROSS_CASES = [
     (1, 1, 2, 45, 1, 72, "bf16"),      # one text token: the output is its V row
     (1, 2, 1, 1, 1, 64, "bf16"),       # one query, one text token
     (1, 1, 1, 3, 1, 64, "f32"),
+    # No bias column (D % 16 == 0) and 65..96 text tokens: four 32-key blocks,
+    # of which the third holds the last real keys and the fourth none.  Keys
+    # from L on must be masked in both (a ones row, D % 32 == 0, would
+    # otherwise count them in the denominator).
+    (2, 3, 2, 415, 69, 96, "bf16"),
+    (1, 2, 1, 100, 96, 64, "bf16"),
+    (1, 1, 1, 64, 65, 32, "bf16"),
+    (1, 1, 2, 50, 80, 128, "bf16"),
+    (1, 2, 1, 40, 70, 48, "bf16"),
 ]
 
 
@@ -152,6 +161,8 @@ MASKED_CROSS_CASES = [
     (2, 1, 1, 90, 120, 72, (120, 120), "bf16"),  # nothing padded: the single-launch path
     (3, 1, 1, 70, 33, 8, (33, 2, 17), "bf16"),
     (2, 4, 4, 64, 16, 64, (16, 5), "f32"),       # tiny-config shape
+    (2, 2, 1, 90, 120, 64, (70, 96), "bf16"),    # no bias column, 65..96 real tokens
+    (2, 1, 1, 60, 100, 96, (65, 100), "bf16"),
 ]
 
 

@@ -19,7 +19,7 @@ from reuse_pab_plan_amd import lib, synth
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 12
+N_CASES = 24
 HEAD_DIMS = list(range(8, 129, 8))
 
 
