@@ -222,18 +222,32 @@ def test_custom_scale():
     assert_close(o, ref, "bf16", "spatial scale=0.05")
 
 
-def test_large_logits_stable():
-    # Scores spanning ~1e3 in the log domain: online max and lazy rescale.
+LARGE_LOGIT_CASES = [
+    # kind, B x H x F x S x D, text tokens, multiplier on Q
+    ("spatial", (1, 1, 1, 700, 64), None, 6.0),    # online max and lazy rescale
+    ("spatial", (1, 2, 2, 333, 72), None, 30.0),
+    ("temporal", (1, 2, 48, 37, 72), None, 30.0),  # full-row max over the frames
+    ("cross", (1, 2, 2, 150, 64), 100, 30.0),      # no bias column, padded key blocks
+    ("cross", (1, 1, 3, 90, 72), 120, 30.0),       # bias column
+]
+
+
+@pytest.mark.parametrize("case", LARGE_LOGIT_CASES, ids=lambda c: f"{c[0]}-{'x'.join(map(str, c[1]))}")
+def test_large_logits_stable(case):
+    # Scores spanning hundreds to thousands of units in the log domain.
     _dev()
-    q, k, v = inputs((1, 1, 1, 700, 64), "bf16", 9, 0)
-    q = (q.float() * 6).to(torch.bfloat16)
-    ref = oracle.spatial(q, k, v)
+    kind, shape, L, mult = case
+    print(f"[case] large logits {case}", flush=True)
+    kv = (shape[0], shape[1], L, shape[4]) if kind == "cross" else None
+    q, k, v = inputs(shape, "bf16", 9, 0, kv_shape=kv)
+    q = (q.float() * mult).to(torch.bfloat16)
+    ref = getattr(oracle, kind)(q, k, v)
     qd, kd, vd = to_dev(q, k, v)
     o = torch.empty_like(qd)
-    lib.pab_attn_spatial(qd, kd, vd, o)
+    getattr(lib, f"pab_attn_{kind}")(qd, kd, vd, o)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
-    assert_close(o, ref, "bf16", "spatial large logits")
+    assert_close(o, ref, "bf16", f"{kind} large logits")
 
 
 def test_determinism_bitwise():
