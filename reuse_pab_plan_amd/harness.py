@@ -255,8 +255,14 @@ class Trajectory:
                        for _ in range(self.T)] for _ in range(cfg.blocks)]
         # Module intermediates (q, k, v, attention output), shared by every
         # (block, type): the dispatches run one after another on one stream.
-        self.mod_scratch = ([torch.empty(cfg.video_shape, dtype=tdt, device=self.device)
-                             for _ in range(4)] if cfg.module else None)
+        # k and v also hold a cross module's projected text, which can be the
+        # larger of the two (more text tokens than video tokens).
+        if cfg.module:
+            nv, nt = int(np.prod(cfg.video_shape)), int(np.prod(cfg.text_shape))
+            self.mod_scratch = [torch.empty(n, dtype=tdt, device=self.device)
+                                for n in (nv, max(nv, nt), max(nv, nt), nv)]
+        else:
+            self.mod_scratch = None
         # Constant text (a module workload with const_text): the text K/V of
         # each block are projected once per trajectory into buffers of their
         # own, and the cross modules read them instead of projecting again.

@@ -172,6 +172,9 @@ MODULE_SHAPES = [
     ("d128", dict(H=2, F=3, S=70, D=128, L=9, N=6, ranges=(1, 2, 3))),
     ("c288_long_text", dict(H=4, F=2, S=130, D=72, L=120, N=5, ranges=(1, 1, 1))),
     ("d32_one_token_off", dict(H=8, F=5, S=33, D=32, L=1, N=4, ranges=(0, 0, 0))),
+    # More text tokens than video tokens: the projected text K/V outgrow an
+    # O-sized scratch buffer.
+    ("text_longer_than_video", dict(H=8, F=1, S=40, D=32, L=66, N=4, ranges=(1, 0, 2))),
 ]
 
 
