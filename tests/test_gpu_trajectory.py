@@ -52,10 +52,11 @@ def _sample_check(cfg, kind, q, k, v, out, label):
         nq = F * S
         rows = np.arange(0, nq, max(1, nq // 1000))
         n_text = cfg.text_len[0] if cfg.text_len else None
-        ref = oracle.cross_rows(host(q.view(B, H, nq, D)[0, 1][None, None]),
-                                host(k[0, 1][None, None]), host(v[0, 1][None, None]), 0, 0, rows,
+        hh = min(1, H - 1)  # the second head, where there is one
+        ref = oracle.cross_rows(host(q.view(B, H, nq, D)[0, hh][None, None]),
+                                host(k[0, hh][None, None]), host(v[0, hh][None, None]), 0, 0, rows,
                                 n_text=n_text)
-        got = host(out.view(B, H, nq, D)[0, 1])[rows]
+        got = host(out.view(B, H, nq, D)[0, hh])[rows]
         if cfg.text_len:
             # Every other entry, sampled too (its own number of text tokens).
             for b in range(1, B):
