@@ -346,3 +346,36 @@ def test_f32_path_ignores_stale_lds(D):
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
     assert_close(o, ref, "f32", f"spatial {case} after NaN LDS")
+
+
+def test_cross_text_length_grid():
+    # Text lengths around the 32-key block edges (1, 2 or 4 key blocks, the
+    # last one or two partly or wholly padding) for head widths with and
+    # without a bias column (D % 16) and a ones column (D % 32), plain and
+    # padded prompts (padding rows NaN / huge on the device: never read).
+    _dev()
+    failures = []
+    for D in (16, 32, 48, 64, 96, 128):
+        for L in (31, 33, 64, 65, 70, 96, 97):
+            B, H, F, S = 2, 1, 1, 70
+            q, k, v = inputs((B, H, F, S, D), "bf16", 31, 2, kv_shape=(B, H, L, D))
+            for lens in (None, (L, max(1, L - 7))):
+                ref = oracle.cross(q, k, v, text_len=lens)
+                qd, kd, vd = to_dev(q, k, v)
+                o = torch.empty_like(qd)
+                if lens is None:
+                    lib.pab_attn_cross(qd, kd, vd, o)
+                else:
+                    for b, n in enumerate(lens):
+                        kd[b, :, n:] = float("nan")
+                        vd[b, :, n:] = 1e30
+                    lib.pab_attn_cross_masked(qd, kd, vd, o, lens)
+                torch.cuda.synchronize()
+                got = o.detach().cpu().double().numpy()
+                err = got - np.asarray(ref, np.float64)
+                mx = float(np.abs(err).max())
+                rl = float(np.linalg.norm(err) / np.linalg.norm(ref))
+                if not (np.isfinite(got).all() and mx <= 2e-2 and rl <= 5e-3):
+                    failures.append((D, L, lens, mx, rl))
+    print(f"[parity] cross text-length grid: {len(failures)} failures", flush=True)
+    assert not failures, failures
