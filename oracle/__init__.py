@@ -44,6 +44,7 @@ from .schedule import (  # noqa: F401
     schedule,
     closed_form_counts,
     calibrate_ranges,
+    calibrate_ranges_stack,
 )
 from .attention import (  # noqa: F401
     attn_loop,

@@ -151,10 +151,28 @@ def calibrate_ranges(diff, candidates, lo_pct: int = 15, hi_pct: int = 85):
       (ranges, scores): ranges[a] assigned to type a, and the score of each
       type (Python floats, i.e. fp64).
     """
-    n_steps = len(diff)
+    return calibrate_ranges_stack([diff], candidates, lo_pct, hi_pct)
+
+
+def calibrate_ranges_stack(diffs, candidates, lo_pct: int = 15, hi_pct: int = 85):
+    """``calibrate_ranges`` for a stack of blocks that share one schedule.
+
+    Reading 7 (the pages calibrate a model, not a block): every block of a
+    stack follows the same schedule, so a type's score is the mean of its
+    counted differences over all blocks -- the sum runs block by block, each
+    block's counted steps in step order, in fp64, and is divided by
+    (blocks x counted steps).  One block is ``calibrate_ranges``.
+
+    Args:
+      diffs: [blocks][N][T] numbers, one ``calibrate_ranges`` matrix per block.
+    """
+    n_blocks = len(diffs)
     n_types = len(candidates)
-    if n_steps < 1 or n_types < 1:
-        raise ValueError("need at least one step and one type")
+    if n_blocks < 1 or n_types < 1:
+        raise ValueError("need at least one block and one type")
+    n_steps = len(diffs[0])
+    if n_steps < 1 or any(len(d) != n_steps for d in diffs):
+        raise ValueError("every block needs the same number (>= 1) of steps")
     if any(int(c) < 0 for c in candidates):
         raise ValueError("candidate ranges must be >= 0")
     if not (0 <= lo_pct <= hi_pct <= 100):
@@ -166,12 +184,13 @@ def calibrate_ranges(diff, candidates, lo_pct: int = 15, hi_pct: int = 85):
     scores = []
     for a in range(n_types):
         total = 0.0
-        for i in counted:
-            d = float(diff[i][a])
-            if not (d >= 0.0) or d == float("inf"):
-                raise ValueError("attention differences must be finite and >= 0")
-            total += d
-        scores.append(total / len(counted))
+        for diff in diffs:
+            for i in counted:
+                d = float(diff[i][a])
+                if not (d >= 0.0) or d == float("inf"):
+                    raise ValueError("attention differences must be finite and >= 0")
+                total += d
+        scores.append(total / (len(counted) * n_blocks))
     # Most-changing type first; it receives the narrowest range.
     order = sorted(range(n_types), key=lambda a: (-scores[a], a))
     ascending = sorted(int(c) for c in candidates)

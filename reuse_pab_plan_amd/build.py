@@ -34,6 +34,7 @@ SOURCES = [
     "temporal.hip",
     "proj.hip",
     "peaks.hip",
+    "synth.hip",
 ]
 
 # Packed fp32 instructions are disabled for all device code on purpose.

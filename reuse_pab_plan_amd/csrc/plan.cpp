@@ -62,15 +62,17 @@ extern "C" int pab_plan_schedule(int32_t num_steps, int32_t num_types, const int
 // "Implementation": each type's range follows how much its output changes
 // between consecutive steps inside the stable window (the less, the wider),
 // that change being the MSE of Figure 1.  A type's score is the mean of its
-// differences over the steps whose output and predecessor's output both lie
-// in the window (summed in step order, fp64); candidates are handed out by
-// rank, the largest score receiving the smallest candidate (ties: the lower
-// type index counts as larger).
-extern "C" int pab_plan_calibrate(int32_t num_steps, int32_t num_types, const double* diff,
-                                  int32_t window_lo_pct, int32_t window_hi_pct,
+// differences over every block and the steps whose output and
+// predecessor's output both lie in the window (summed block by block, each
+// block's steps in step order, fp64); candidates are handed out by rank,
+// the largest score receiving the smallest candidate (ties: the lower type
+// index counts as larger).
+extern "C" int pab_plan_calibrate(int32_t num_blocks, int32_t num_steps, int32_t num_types,
+                                  const double* diff, int32_t window_lo_pct, int32_t window_hi_pct,
                                   const int32_t* candidate_ranges, int32_t* ranges_out,
                                   double* score_out) {
   const char* fn = "pab_plan_calibrate";
+  if (num_blocks < 1) return fail(PAB_ERR_INVALID_ARG, fmt("%s: num_blocks must be >= 1", fn));
   if (num_steps < 1) return fail(PAB_ERR_INVALID_ARG, fmt("%s: num_steps must be >= 1", fn));
   if (num_types < 1 || num_types > 32)
     return fail(PAB_ERR_INVALID_ARG, fmt("%s: num_types must be in [1, 32]", fn));
@@ -85,25 +87,29 @@ extern "C" int pab_plan_calibrate(int32_t num_steps, int32_t num_types, const do
   auto inside = [&](int64_t i) {
     return 100 * i >= (int64_t)window_lo_pct * n && 100 * i < (int64_t)window_hi_pct * n;
   };
-  double score[32];
   int64_t counted = 0;
-  for (int a = 0; a < num_types; ++a) score[a] = 0.0;
-  for (int64_t i = 1; i < n; ++i) {
-    if (!(inside(i) && inside(i - 1))) continue;
-    ++counted;
-    for (int a = 0; a < num_types; ++a) {
-      const double d = diff[i * num_types + a];
-      if (!(d >= 0.0) || d == std::numeric_limits<double>::infinity())
-        return fail(PAB_ERR_INVALID_ARG,
-                    fmt("%s: difference at step %lld, type %d is not finite and >= 0", fn,
-                        (long long)i, a));
-      score[a] += d;
-    }
-  }
+  for (int64_t i = 1; i < n; ++i)
+    if (inside(i) && inside(i - 1)) ++counted;
   if (counted == 0)
     return fail(PAB_ERR_INVALID_ARG,
                 fmt("%s: the window holds no two consecutive steps", fn));
-  for (int a = 0; a < num_types; ++a) score[a] /= (double)counted;
+  double score[32];
+  for (int a = 0; a < num_types; ++a) score[a] = 0.0;
+  for (int64_t b = 0; b < num_blocks; ++b) {
+    const double* db = diff + b * n * num_types;
+    for (int64_t i = 1; i < n; ++i) {
+      if (!(inside(i) && inside(i - 1))) continue;
+      for (int a = 0; a < num_types; ++a) {
+        const double d = db[i * num_types + a];
+        if (!(d >= 0.0) || d == std::numeric_limits<double>::infinity())
+          return fail(PAB_ERR_INVALID_ARG,
+                      fmt("%s: difference at block %lld, step %lld, type %d is not finite and >= 0",
+                          fn, (long long)b, (long long)i, a));
+        score[a] += d;
+      }
+    }
+  }
+  for (int a = 0; a < num_types; ++a) score[a] /= (double)(counted * num_blocks);
 
   // Rank: largest score first, lower index first among equals.
   int order[32];

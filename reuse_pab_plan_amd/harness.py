@@ -160,11 +160,14 @@ def mse_bytes(cfg: Config) -> int:
 class Inputs:
     """Per (block, type, step) Q/K/V device tensors (module configurations:
     the module input x, plus the text tokens for a cross attention, and fixed
-    projection weights per (block, type)).
+    projection weights per (block, type)), drawn by the device generator.
 
     resident=True generates every needed step up front (the timed region then
-    only reads HBM); otherwise tensors are generated on demand, outside the
-    timed brackets, into reusable buffers.
+    only reads HBM).  Otherwise tensors are generated on demand into a ring of
+    two buffer sets: ``get(..., ahead=next)`` returns a step's tensors and
+    also draws the next recompute's into the other set, so a kernel never
+    reads inputs that were the last thing written (they would still sit in
+    the 256 MB Infinity Cache).
     """
 
     def __init__(self, cfg: Config, steps_needed, device="cuda", resident=True):
@@ -173,8 +176,10 @@ class Inputs:
         self.cfg, self.device, self.resident = cfg, device, resident
         self.tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.store = {}
-        self.scratch = {}
         self._w = {}
+        self._ring = None
+        self._ring_key = [None, None]
+        self._last = 1
         if resident:
             for (b, a, i) in steps_needed:
                 self.store[(b, a, i)] = self._make(b, a, i, None)
@@ -209,21 +214,48 @@ class Inputs:
         # Module inputs use their own generator streams (tensors 3 and 4).
         first = 3 if self.cfg.module else 0
         for tensor, shape in enumerate(shapes, start=first):
-            dst = None if out is None else out[tensor]
+            dst = None if out is None else out[tensor - first]
             res.append(synth.gpu_tensor(shape, self.cfg.seed, b, t, tensor, i, self.cfg.N,
                                         self.cfg.dtype, self.device, out=dst,
                                         perturb=not (const and tensor != first)))
         return tuple(res)
 
-    def get(self, b, a, i):
-        if self.resident:
-            return self.store[(b, a, i)]
+    def _ring_views(self, slot, a):
         import torch
 
-        if a not in self.scratch:
-            self.scratch[a] = tuple(torch.empty(s, dtype=self.tdt, device=self.device)
-                                    for s in self._shapes(a))
-        return self._make(b, a, i, self.scratch[a])
+        if self._ring is None:
+            # Each set: one flat buffer per tensor position, as large as the
+            # largest tensor any type puts there.
+            sizes = [0, 0, 0]
+            for a2 in range(len(self.cfg.kinds)):
+                for j, shp in enumerate(self._shapes(a2)):
+                    sizes[j] = max(sizes[j], int(np.prod(shp)))
+            self._ring = [[torch.empty(n, dtype=self.tdt, device=self.device) if n else None
+                           for n in sizes] for _ in range(2)]
+        return tuple(self._ring[slot][j][:int(np.prod(shp))].view(shp)
+                     for j, shp in enumerate(self._shapes(a)))
+
+    def _gen(self, key, slot):
+        b, a, i = key
+        self._make(b, a, i, self._ring_views(slot, a))
+        self._ring_key[slot] = key
+
+    def get(self, b, a, i, ahead=None):
+        """The tensors of (block b, type a, step i); with ``ahead`` = the
+        (block, type, step) of the next recompute (streamed inputs only), that
+        one is drawn too, into the other buffer set."""
+        if self.resident:
+            return self.store[(b, a, i)]
+        key = (b, a, i)
+        if key in self._ring_key:
+            slot = self._ring_key.index(key)
+        else:
+            slot = 1 - self._last
+            self._gen(key, slot)
+        if ahead is not None and ahead not in self._ring_key and ahead != key:
+            self._gen(ahead, 1 - slot)
+        self._last = slot
+        return self._ring_views(slot, a)
 
 
 # --------------------------------------------------------------- trajectory
@@ -335,15 +367,22 @@ class Trajectory:
         done = np.zeros((cfg.blocks, self.T), dtype=bool)  # a recompute happened this run
         mk = (lambda: torch.cuda.Event(enable_timing=True)) if events else None
         text_done = set()  # blocks whose constant text K/V this run has projected
+        n_run = cfg.N if max_steps is None else min(max_steps, cfg.N)
+        # The recomputes in run order: with streamed inputs each one draws
+        # the next one's inputs ahead of its own dispatch.
+        order = [(b, a, i) for i in range(n_run) for b in range(cfg.blocks)
+                 for a in range(self.T) if self.recompute[i, a]]
+        ahead = dict(zip(order, order[1:]))
         with torch.cuda.stream(self.stream):
-            for i in range(cfg.N if max_steps is None else min(max_steps, cfg.N)):
+            for i in range(n_run):
                 for b in range(cfg.blocks):
                     for a in range(self.T):
                         d = self._descs[b][a]
                         t = self._types[b * self.T + a]
                         rec = bool(self.recompute[i, a])
+                        nxt = ahead.get((b, a, i))
                         if rec and cfg.module:
-                            x = self.inputs.get(b, a, i)
+                            x = self.inputs.get(b, a, i, ahead=nxt)
                             w_in, w_kv, w_out = self.inputs.weights(b, a)
                             t[0].x = x[0].data_ptr()
                             t[0].x_text = x[1].data_ptr() if len(x) > 1 else None
@@ -358,7 +397,7 @@ class Trajectory:
                                 t[0].x_text = None
                                 t[0].scratch[1], t[0].scratch[2] = tk.data_ptr(), tv.data_ptr()
                         elif rec:
-                            q, k, v = self.inputs.get(b, a, i)
+                            q, k, v = self.inputs.get(b, a, i, ahead=nxt)
                             t[0].q, t[0].k, t[0].v = q.data_ptr(), k.data_ptr(), v.data_ptr()
                         # With drift on, the dispatcher itself takes the
                         # attention difference of each recompute against the
@@ -398,29 +437,32 @@ class Trajectory:
 
 # --------------------------------------------------------------- calibration
 
-def calibrate(traj: Trajectory, candidate_ranges=None):
+def calibrate(traj: Trajectory, candidate_ranges=None, rerun: bool = True):
     """Broadcast ranges from a profiling trajectory's attention difference.
 
     ``traj`` must be a PAB-off trajectory (every step computes) with inputs
-    attached; it is run once with the attention-difference MSE after every
-    step (the Figure 1 quantity, averaged over blocks), and
-    ``pab_plan_calibrate`` turns the differences into per-type ranges, the
+    attached.  With ``rerun`` it is run once with the attention-difference
+    MSE after every step (the Figure 1 quantity); otherwise the differences
+    its last drift-on run left in ``traj.drift_out`` are used.
+    ``pab_plan_calibrate`` turns every block's differences into per-type
+    ranges (scores averaged over the blocks, which share one schedule), the
     candidates (default: the configuration's ranges) handed out by rank.
-    Returns (ranges, scores, diff[N, T]).
+    Returns (ranges, scores, diff[blocks, N, T]).
     """
     import torch
 
     if traj.pab:
         raise ValueError("calibration needs a trajectory that computes every step")
     cfg = traj.cfg
-    keep = traj.drift
-    traj.drift = True
-    try:
-        traj.run(events=False)
-    finally:
-        traj.drift = keep
+    if rerun:
+        keep = traj.drift
+        traj.drift = True
+        try:
+            traj.run(events=False)
+        finally:
+            traj.drift = keep
     torch.cuda.synchronize(traj.device)
-    diff = traj.drift_out.mean(dim=0).transpose(0, 1).contiguous().cpu().numpy()
+    diff = traj.drift_out.transpose(1, 2).contiguous().cpu().numpy()
     cand = list(cfg.ranges) if candidate_ranges is None else list(candidate_ranges)
     ranges, scores = lib.pab_plan_calibrate(diff, cand)
     return ranges, scores, diff

@@ -57,6 +57,13 @@ EXPORTED_PEAKS = (
     "pab_peak_exp",
 )
 
+# Workload generator (include/pab_synth.h): seeded synthetic inputs, not part
+# of the method.
+EXPORTED_SYNTH = (
+    "pab_synth_philox",
+    "pab_synth_normal",
+)
+
 
 class PabError(RuntimeError):
     def __init__(self, fn, status, msg):
@@ -120,7 +127,7 @@ def load(path: str = LIB_PATH):
     lib.pab_plan_schedule.argtypes = [i32, i32, C.POINTER(i32), i32, i32,
                                       C.POINTER(C.c_uint8), C.POINTER(i32), C.POINTER(i32)]
     lib.pab_plan_schedule.restype = C.c_int
-    lib.pab_plan_calibrate.argtypes = [i32, i32, C.POINTER(C.c_double), i32, i32,
+    lib.pab_plan_calibrate.argtypes = [i32, i32, i32, C.POINTER(C.c_double), i32, i32,
                                        C.POINTER(i32), C.POINTER(i32), C.POINTER(C.c_double)]
     lib.pab_plan_calibrate.restype = C.c_int
     for name in ("pab_attn_spatial", "pab_attn_temporal"):
@@ -147,6 +154,10 @@ def load(path: str = LIB_PATH):
     lib.pab_last_error.restype = C.c_char_p
     lib.pab_version.argtypes = []
     lib.pab_version.restype = C.c_char_p
+    lib.pab_synth_philox.argtypes = [vp, i64, C.c_uint64, C.c_uint64, vp]
+    lib.pab_synth_philox.restype = C.c_int
+    lib.pab_synth_normal.argtypes = [vp, i64, i32, C.c_uint64, f32, C.c_uint64, f32, vp]
+    lib.pab_synth_normal.restype = C.c_int
     lib.pab_peak_sink_bytes.argtypes = []
     lib.pab_peak_sink_bytes.restype = sz
     lib.pab_peak_copy.argtypes = [vp, vp, sz, vp]
@@ -194,18 +205,23 @@ def pab_plan_schedule(num_steps: int, ranges, window_lo_pct: int = 15, window_hi
 
 
 def pab_plan_calibrate(diff, candidate_ranges, window_lo_pct: int = 15, window_hi_pct: int = 85):
-    """diff: [N, T] attention differences (row i: steps i-1 -> i).
+    """diff: [N, T] attention differences of one block (row i: steps i-1 ->
+    i), or [blocks, N, T] for a stack sharing one schedule.
     Returns (ranges int32 [T], scores float64 [T])."""
     lib = load()
     d = np.ascontiguousarray(np.asarray(diff, dtype=np.float64))
-    n, t = d.shape
+    if d.ndim == 2:
+        d = d[None]
+    if d.ndim != 3:
+        raise ValueError("diff must be [N, T] or [blocks, N, T]")
+    nb, n, t = d.shape
     c = np.ascontiguousarray(np.asarray(candidate_ranges, dtype=np.int32))
     if c.shape != (t,):
         raise ValueError("one candidate range per attention type")
     out = np.zeros(t, dtype=np.int32)
     sc = np.zeros(t, dtype=np.float64)
     st = lib.pab_plan_calibrate(
-        n, t, d.ctypes.data_as(C.POINTER(C.c_double)), window_lo_pct, window_hi_pct,
+        nb, n, t, d.ctypes.data_as(C.POINTER(C.c_double)), window_lo_pct, window_hi_pct,
         c.ctypes.data_as(C.POINTER(C.c_int32)), out.ctypes.data_as(C.POINTER(C.c_int32)),
         sc.ctypes.data_as(C.POINTER(C.c_double)))
     _check("pab_plan_calibrate", st)
@@ -236,8 +252,55 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr())
 
 
+def _bad(fn, msg):
+    raise PabError(fn, PAB_ERR_INVALID_ARG, msg)
+
+
+def _dense(fn, **tensors):
+    """Each tensor must be contiguous (the library takes a bare pointer and
+    assumes the documented dense layout) and on the GPU."""
+    for name, t in tensors.items():
+        if t is None:
+            _bad(fn, f"{name} is None")
+        if not t.is_contiguous():
+            _bad(fn, f"{name} must be contiguous (a strided view would be read as dense)")
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            _bad(fn, f"{name} must be a device tensor")
+
+
+def _same(fn, ref_name, ref, **tensors):
+    """Every tensor has the reference's shape and dtype."""
+    for name, t in tensors.items():
+        if tuple(t.shape) != tuple(ref.shape):
+            _bad(fn, f"{name} has shape {tuple(t.shape)}, {ref_name} {tuple(ref.shape)}")
+        if t.dtype != ref.dtype:
+            _bad(fn, f"{name} has dtype {t.dtype}, {ref_name} {ref.dtype}")
+
+
+def _video_attn_args(fn, q, k, v, o):
+    if q.dim() != 5:
+        _bad(fn, f"q must be [B, H, F, S, D], got {tuple(q.shape)}")
+    _same(fn, "q", q, k=k, v=v, o=o)
+    _dense(fn, q=q, k=k, v=v, o=o)
+
+
+def _cross_args(fn, q, k_text, v_text, o):
+    if q.dim() < 3:
+        _bad(fn, f"q must be [B, H, ..., D], got {tuple(q.shape)}")
+    _same(fn, "q", q, o=o)
+    _same(fn, "k_text", k_text, v_text=v_text)
+    B, H, D = q.shape[0], q.shape[1], q.shape[-1]
+    if k_text.dim() != 4 or (k_text.shape[0], k_text.shape[1], k_text.shape[3]) != (B, H, D):
+        _bad(fn, f"k_text must be [B, H, L, D] = [{B}, {H}, L, {D}], got {tuple(k_text.shape)}")
+    if k_text.dtype != q.dtype:
+        _bad(fn, f"k_text has dtype {k_text.dtype}, q {q.dtype}")
+    _dense(fn, q=q, k_text=k_text, v_text=v_text, o=o)
+
+
 def pab_attn_spatial(q, k, v, o, softmax_scale: float = 0.0, stream=None):
     """q, k, v, o: [B, H, F, S, D] device tensors (bf16 or fp32)."""
+    _video_attn_args("pab_attn_spatial", q, k, v, o)
     B, H, F, S, D = q.shape
     st = load().pab_attn_spatial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, F, S, D,
                                  _dtype_code(q), softmax_scale, _stream_ptr(stream))
@@ -247,6 +310,7 @@ def pab_attn_spatial(q, k, v, o, softmax_scale: float = 0.0, stream=None):
 
 def pab_attn_temporal(q, k, v, o, softmax_scale: float = 0.0, stream=None):
     """q, k, v, o: [B, H, F, S, D] device tensors (bf16 or fp32)."""
+    _video_attn_args("pab_attn_temporal", q, k, v, o)
     B, H, F, S, D = q.shape
     st = load().pab_attn_temporal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, F, S, D,
                                   _dtype_code(q), softmax_scale, _stream_ptr(stream))
@@ -256,6 +320,7 @@ def pab_attn_temporal(q, k, v, o, softmax_scale: float = 0.0, stream=None):
 
 def pab_attn_cross(q, k_text, v_text, o, softmax_scale: float = 0.0, stream=None):
     """q, o: [B, H, ..., D] video queries; k_text, v_text: [B, H, L, D]."""
+    _cross_args("pab_attn_cross", q, k_text, v_text, o)
     B, H = q.shape[0], q.shape[1]
     D = q.shape[-1]
     nq = q.numel() // (B * H * D)
@@ -268,6 +333,7 @@ def pab_attn_cross(q, k_text, v_text, o, softmax_scale: float = 0.0, stream=None
 
 def pab_attn_cross_masked(q, k_text, v_text, o, text_len, softmax_scale: float = 0.0, stream=None):
     """As pab_attn_cross; batch entry b attends to its first text_len[b] text tokens."""
+    _cross_args("pab_attn_cross_masked", q, k_text, v_text, o)
     B, H = q.shape[0], q.shape[1]
     D = q.shape[-1]
     nq = q.numel() // (B * H * D)
@@ -284,7 +350,22 @@ def pab_attn_cross_masked(q, k_text, v_text, o, text_len, softmax_scale: float =
 
 def pab_proj_in(x, w, outs, frames: int, tokens: int, heads: int, head_dim: int, stream=None):
     """x: [B, F*S, C] token-major; w: [n*C, C]; outs: n head-major tensors [B, H, F, S, D]."""
+    fn = "pab_proj_in"
     n = len(outs)
+    if not 1 <= n <= 3:
+        _bad(fn, "one to three output tensors")
+    C_ = heads * head_dim
+    if x.dim() != 3 or x.shape[1] != frames * tokens or x.shape[2] != C_:
+        _bad(fn, f"x must be [B, F*S, H*D] = [B, {frames * tokens}, {C_}], got {tuple(x.shape)}")
+    if tuple(w.shape) != (n * C_, C_):
+        _bad(fn, f"w must be [{n * C_}, {C_}], got {tuple(w.shape)}")
+    want = x.shape[0] * heads * frames * tokens * head_dim
+    for j, t in enumerate(outs):
+        if t.numel() != want or t.dtype != x.dtype:
+            _bad(fn, f"out{j} must hold {want} elements of {x.dtype}")
+    if w.dtype != x.dtype:
+        _bad(fn, f"w has dtype {w.dtype}, x {x.dtype}")
+    _dense(fn, x=x, w=w, **{f"out{j}": t for j, t in enumerate(outs)})
     ptrs = [_ptr(t) for t in outs] + [None] * (3 - n)
     st = load().pab_proj_in(_ptr(x), _ptr(w), ptrs[0], ptrs[1], ptrs[2], n, x.shape[0], frames,
                             tokens, heads, head_dim, _dtype_code(x), _stream_ptr(stream))
@@ -294,7 +375,15 @@ def pab_proj_in(x, w, outs, frames: int, tokens: int, heads: int, head_dim: int,
 
 def pab_proj_out(o, w, y, stream=None):
     """o: [B, H, F, S, D] head-major; w: [C, C]; y: [B, F*S, C] token-major."""
+    fn = "pab_proj_out"
+    if o.dim() != 5:
+        _bad(fn, f"o must be [B, H, F, S, D], got {tuple(o.shape)}")
     B, H, F, S, D = o.shape
+    if tuple(w.shape) != (H * D, H * D) or w.dtype != o.dtype:
+        _bad(fn, f"w must be [{H * D}, {H * D}] of {o.dtype}")
+    if y.numel() != o.numel() or y.dtype != o.dtype:
+        _bad(fn, f"y must hold {o.numel()} elements of {o.dtype}")
+    _dense(fn, o=o, w=w, y=y)
     st = load().pab_proj_out(_ptr(o), _ptr(w), _ptr(y), B, F, S, H, D, _dtype_code(o),
                              _stream_ptr(stream))
     _check("pab_proj_out", st)
@@ -307,6 +396,14 @@ def pab_mse_workspace_bytes(n: int) -> int:
 
 def pab_attn_diff_mse(a, b, out, workspace, stream=None):
     """out: 1-element float64 device tensor; workspace: device buffer (uint8)."""
+    import torch
+
+    fn = "pab_attn_diff_mse"
+    if a.numel() != b.numel() or a.dtype != b.dtype:
+        _bad(fn, "a and b must have the same number of elements and dtype")
+    if out.dtype != torch.float64 or out.numel() < 1:
+        _bad(fn, "out must be a float64 tensor of at least one element")
+    _dense(fn, a=a, b=b, out=out, workspace=workspace)
     n = a.numel()
     st = load().pab_attn_diff_mse(_ptr(a), _ptr(b), n, _dtype_code(a), _ptr(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream_ptr(stream))
@@ -321,6 +418,31 @@ def pab_step_dispatch(desc: StepDesc, step: int):
     st = load().pab_step_dispatch(C.byref(desc), step, C.byref(mask), outs)
     _check("pab_step_dispatch", st)
     return mask.value, [outs[a] for a in range(desc.num_types)]
+
+
+# ---------------------------------------------------------- workload generator
+
+def pab_synth_philox(out, key: int, block0: int = 0, stream=None):
+    """out: int32 device tensor of 4*nblocks elements (the uint32 words, as
+    bits): words of Philox4x32-10 blocks block0.. of stream ``key``."""
+    fn = "pab_synth_philox"
+    if out.element_size() != 4 or out.numel() % 4:
+        _bad(fn, "out must hold a multiple of four 32-bit words")
+    _dense(fn, out=out)
+    st = load().pab_synth_philox(_ptr(out), out.numel() // 4, key, block0, _stream_ptr(stream))
+    _check(fn, st)
+    return out
+
+
+def pab_synth_normal(out, key_a: int, scale_a: float, key_b: int = 0, scale_b: float = 0.0,
+                     stream=None):
+    """out (bf16 or fp32 device tensor) = round(scale_a N(key_a) + scale_b N(key_b))."""
+    fn = "pab_synth_normal"
+    _dense(fn, out=out)
+    st = load().pab_synth_normal(_ptr(out), out.numel(), _dtype_code(out), key_a, scale_a, key_b,
+                                 scale_b, _stream_ptr(stream))
+    _check(fn, st)
+    return out
 
 
 # ------------------------------------------------------------ measurement aids

@@ -19,6 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH), reason="libpab
 
 
 PEAKS_HEADER = os.path.join(ROOT, "include", "pab_peaks.h")
+SYNTH_HEADER = os.path.join(ROOT, "include", "pab_synth.h")
 
 
 def declared_functions(header=HEADER):
@@ -33,7 +34,9 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lib.EXPORTED)
     peaks = declared_functions(PEAKS_HEADER)
     assert set(peaks) == set(lib.EXPORTED_PEAKS)
-    for name in names + peaks:
+    synth_fns = declared_functions(SYNTH_HEADER)
+    assert set(synth_fns) == set(lib.EXPORTED_SYNTH)
+    for name in names + peaks + synth_fns:
         assert hasattr(L, name), name
     assert "gfx950" in lib.pab_version()
 

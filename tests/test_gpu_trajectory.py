@@ -300,7 +300,8 @@ def test_range_calibration_matches_oracle():
     traj = harness.Trajectory(cfg, pab=False, device=dev)
     traj.inputs = harness.Inputs(cfg, traj.steps_needed(), device=dev)
     ranges, scores, diff = harness.calibrate(traj)
-    want_r, want_s = oracle.calibrate_ranges(diff.tolist(), list(cfg.ranges))
+    assert diff.shape == (1, cfg.N, len(cfg.kinds))
+    want_r, want_s = oracle.calibrate_ranges(diff[0].tolist(), list(cfg.ranges))
     assert list(ranges) == want_r and list(scores) == want_s
 
     host = lambda t: t.detach().cpu().numpy()

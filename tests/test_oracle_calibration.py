@@ -33,10 +33,13 @@ def _load():
         if tok[0] == "case":
             kv = dict(t.split("=") for t in tok[2:])
             cur = {"name": tok[1], "N": int(kv["N"]), "lo": int(kv["lo"]), "hi": int(kv["hi"]),
-                   "cand": [int(x) for x in kv["candidates"].split(",")], "diff": {}}
+                   "cand": [int(x) for x in kv["candidates"].split(",")], "diff": {},
+                   "blocks": int(kv.get("blocks", "1"))}
             cases.append(cur)
         elif tok[0] == "diff":
-            cur["diff"][tok[1]] = [float(x) for x in tok[2:]]
+            # "diff <type>" (block 0) or "diff <type>/<block>"
+            name, _, blk = tok[1].partition("/")
+            cur["diff"][(name, int(blk or 0))] = [float(x) for x in tok[2:]]
         elif tok[0] == "expect":
             if tok[1] == "error":
                 cur["error"] = True
@@ -47,32 +50,58 @@ def _load():
     return cases
 
 
-def _matrix(case):
-    names = [t for t in TYPES if t in case["diff"]]
-    return [[case["diff"][t][i] for t in names] for i in range(case["N"])]
+def _matrix(case, block=0):
+    names = [t for t in TYPES if (t, block) in case["diff"]]
+    return [[case["diff"][(t, block)][i] for t in names] for i in range(case["N"])]
+
+
+def _stack(case):
+    return [_matrix(case, b) for b in range(case["blocks"])]
 
 
 @pytest.mark.parametrize("case", _load(), ids=lambda c: c["name"])
 def test_oracle_hand_cases(case):
-    diff = _matrix(case)
-    assert all(len(case["diff"][t]) == case["N"] for t in case["diff"])
+    assert all(len(v) == case["N"] for v in case["diff"].values())
+    assert len({k[1] for k in case["diff"]}) == case["blocks"]
+    fn = (lambda: oracle.calibrate_ranges(_matrix(case), case["cand"], case["lo"], case["hi"])) \
+        if case["blocks"] == 1 else \
+        (lambda: oracle.calibrate_ranges_stack(_stack(case), case["cand"], case["lo"], case["hi"]))
     if case.get("error"):
         with pytest.raises(ValueError):
-            oracle.calibrate_ranges(diff, case["cand"], case["lo"], case["hi"])
+            fn()
         return
-    ranges, scores = oracle.calibrate_ranges(diff, case["cand"], case["lo"], case["hi"])
+    ranges, scores = fn()
     assert ranges == case["ranges"]
     assert scores == case["scores"]
 
 
+def test_stack_of_one_is_single_block():
+    for case in _load():
+        if case["blocks"] == 1 and not case.get("error"):
+            assert oracle.calibrate_ranges_stack([_matrix(case)], case["cand"], case["lo"],
+                                                 case["hi"]) == \
+                oracle.calibrate_ranges(_matrix(case), case["cand"], case["lo"], case["hi"])
+
+
+def test_stack_of_identical_blocks_is_one_block():
+    # The mean over blocks of identical differences is the one block's mean
+    # (exactly, for these dyadic values).
+    rng = np.random.default_rng(3)
+    diff = (rng.integers(0, 64, (30, 3)) / 64.0).tolist()
+    one = oracle.calibrate_ranges(diff, [2, 4, 6])
+    assert oracle.calibrate_ranges_stack([diff] * 4, [2, 4, 6]) == one
+
+
 def c_calibrate(diff, cand, lo=15, hi=85):
     d = np.ascontiguousarray(np.asarray(diff, dtype=np.float64))
-    n, t = d.shape
+    if d.ndim == 2:
+        d = d[None]
+    nb, n, t = d.shape
     c = np.ascontiguousarray(np.asarray(cand, dtype=np.int32))
     out = np.zeros(t, dtype=np.int32)
     sc = np.zeros(t, dtype=np.float64)
     st = lib.load().pab_plan_calibrate(
-        n, t, d.ctypes.data_as(C.POINTER(C.c_double)), lo, hi,
+        nb, n, t, d.ctypes.data_as(C.POINTER(C.c_double)), lo, hi,
         c.ctypes.data_as(C.POINTER(C.c_int32)), out.ctypes.data_as(C.POINTER(C.c_int32)),
         sc.ctypes.data_as(C.POINTER(C.c_double)))
     return st, out.tolist(), sc.tolist()
@@ -80,7 +109,7 @@ def c_calibrate(diff, cand, lo=15, hi=85):
 
 @pytest.mark.parametrize("case", _load(), ids=lambda c: c["name"])
 def test_c_planner_hand_cases(case):
-    st, ranges, scores = c_calibrate(_matrix(case), case["cand"], case["lo"], case["hi"])
+    st, ranges, scores = c_calibrate(_stack(case), case["cand"], case["lo"], case["hi"])
     if case.get("error"):
         assert st == lib.PAB_ERR_INVALID_ARG
         return
@@ -153,4 +182,30 @@ def test_c_validation():
     ok[0, 0] = np.nan
     assert c_calibrate(ok, [2, 4, 6])[0] == lib.PAB_OK
     assert c_calibrate(d, [2, 4, 6], lo=50, hi=40)[0] == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_plan_calibrate(10, 3, None, 15, 85, None, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_calibrate(1, 10, 3, None, 15, 85, None, None, None) == lib.PAB_ERR_INVALID_ARG
+    # No blocks; a bad value in the second block's window.
+    dd = np.ascontiguousarray(np.ones((2, 10, 3)))
+    c = np.ascontiguousarray(np.array([2, 4, 6], dtype=np.int32))
+    out = np.zeros(3, dtype=np.int32)
+    args = (dd.ctypes.data_as(C.POINTER(C.c_double)), 15, 85,
+            c.ctypes.data_as(C.POINTER(C.c_int32)), out.ctypes.data_as(C.POINTER(C.c_int32)), None)
+    assert L.pab_plan_calibrate(0, 10, 3, *args) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_plan_calibrate(2, 10, 3, *args) == lib.PAB_OK
+    dd[1, 4, 2] = np.nan
+    assert L.pab_plan_calibrate(2, 10, 3, *args) == lib.PAB_ERR_INVALID_ARG
+    assert "block 1" in lib.pab_last_error()
+    assert L.pab_plan_calibrate(1, 10, 3, *args) == lib.PAB_OK  # block 1 not read
+
+
+def test_c_matches_oracle_random_stacks():
+    rng = np.random.default_rng(12)
+    for trial in range(100):
+        nb = int(rng.integers(1, 5))
+        n = int(rng.integers(3, 40))
+        t = int(rng.integers(1, 5))
+        diff = rng.random((nb, n, t)) * (10.0 ** rng.integers(-8, 3))
+        cand = rng.integers(0, 9, size=t).tolist()
+        want = oracle.calibrate_ranges_stack(diff.tolist(), cand)
+        st, ranges, scores = c_calibrate(diff, cand)
+        assert st == lib.PAB_OK
+        assert ranges == want[0] and scores == want[1]
