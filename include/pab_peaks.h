@@ -23,19 +23,25 @@ extern "C" {
 size_t pab_peak_sink_bytes(void);
 
 /*
- * Plain copy dst[0..bytes) = src[0..bytes): 16-byte non-temporal loads and
- * stores over a fixed grid.  Moves 2*bytes through HBM when neither buffer
- * is cache resident (rotate over buffers larger than the 256 MB Infinity
- * Cache to measure HBM).  bytes: positive multiple of 16; src, dst 16-byte
- * aligned and disjoint (else PAB_ERR_INVALID_ARG).
+ * HBM streaming microbenchmark: one pass over n_src source and n_dst
+ * destination buffers of `bytes` each, in 16-byte vectors: dst_j[i] = XOR
+ * of src_0..src_{n_src-1}[i] (of the vector index when n_src = 0); with
+ * n_dst = 0 the XOR is folded into one word per block written to sink.
+ * Moves (n_src + n_dst) * bytes through HBM when no buffer is cache
+ * resident (use buffers much larger than the 256 MB Infinity Cache, or
+ * rotate).  A grid-stride loop over `blocks` blocks of 256 threads keeps
+ * four vectors of every stream in flight per thread; variant 0 uses plain
+ * loads and stores, 1 non-temporal ones.  The caller picks the best grid
+ * and variant for each read/write mix.
+ * Errors: PAB_ERR_INVALID_ARG for n_src outside [0, 4], n_dst outside
+ *   [0, 2], no stream, NULL/misaligned/overlapping buffers, bytes not a
+ *   positive multiple of 16, blocks outside [1, 65536] or a variant other
+ *   than 0 or 1; PAB_ERR_CAPACITY for a sink (n_dst = 0) smaller than
+ *   pab_peak_sink_bytes() or than `blocks` words.
  */
-int pab_peak_copy(const void* src, void* dst, size_t bytes, void* stream);
-
-/*
- * Read-only pass over src[0..bytes) (16-byte non-temporal loads, folded
- * into one word per block written to sink).  Reads `bytes`.
- */
-int pab_peak_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+int pab_peak_stream(const void* const* src, int32_t n_src, void* const* dst, int32_t n_dst,
+                    size_t bytes, int32_t blocks, int32_t variant, void* sink, size_t sink_bytes,
+                    void* stream);
 
 /*
  * Independent chains of v_mfma_f32_32x32x16_bf16 on register operands, eight

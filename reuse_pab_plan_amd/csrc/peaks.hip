@@ -14,47 +14,89 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kStreamBlocks = 8192;   // copy / read grid (the measured sweet spot)
 constexpr int kStreamThreads = 256;
+constexpr int kMaxStreamBlocks = 65536;
 constexpr int kUnroll = 4;
 constexpr int kMfmaBlocks = 2048;     // 4-wave blocks: 32 waves per CU on 256 CUs
 constexpr int kMfmaThreads = 256;
 constexpr int kMfmaChains = 4;        // independent accumulators per wave
 
-// dst[i] = src[i] over n 16-byte vectors, non-temporal on both sides.
-__global__ __launch_bounds__(kStreamThreads) void copy_kernel(const u32x4* __restrict__ src,
-                                                            u32x4* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-  int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
-  }
-  for (; i < n; i += stride) dst[i] = src[i];
+__device__ __forceinline__ u32x4 ld(const u32x4* p, bool nt) {
+  return nt ? __builtin_nontemporal_load(p) : *p;
+}
+__device__ __forceinline__ void st(u32x4* p, u32x4 v, bool nt) {
+  if (nt)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
 }
 
-// One XOR-folded word per block, so the loads cannot be dropped.
-__global__ __launch_bounds__(kStreamThreads) void read_kernel(const u32x4* __restrict__ src, int64_t n,
-                                                            uint32_t* __restrict__ sink) {
+struct StreamArgs {
+  const u32x4* src[4];
+  u32x4* dst[2];
+};
+
+// One pass over n 16-byte vectors of NS source and ND destination streams:
+// dst_j[i] = XOR over the sources of src[i] (or i itself with no source);
+// with no destination the XOR is folded into one word per block.  A
+// grid-stride loop with kUnroll vectors of every stream in flight per
+// thread; whole-vector tails run one vector at a time.
+template <int NS, int ND, bool NT>
+__global__ __launch_bounds__(kStreamThreads) void stream_kernel(StreamArgs a, int64_t n,
+                                                              uint32_t* __restrict__ sink) {
   const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
   int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t w = (uint32_t)(i + u * stride);
+      v[u] = u32x4{w, w, w, w};
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] ^= ld(a.src[s] + i + u * stride, NT);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) st(a.dst[d] + i + u * stride, v[u], NT);
+    if (ND == 0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
   }
-  for (; i < n; i += stride) acc ^= src[i];
-  __shared__ uint32_t red[kStreamThreads];
-  red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
-  __syncthreads();
-  for (int s = kStreamThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+  for (; i < n; i += stride) {
+    const uint32_t w = (uint32_t)i;
+    u32x4 v = {w, w, w, w};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) v ^= a.src[s][i];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) a.dst[d][i] = v;
+    if (ND == 0) acc ^= v;
+  }
+  if (ND == 0) {
+    __shared__ uint32_t red[kStreamThreads];
+    red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
     __syncthreads();
+    for (int s = kStreamThreads / 2; s > 0; s >>= 1) {
+      if ((int)threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
   }
-  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+template <int NS, int ND>
+void launch_stream(const StreamArgs& a, int64_t n, int blocks, bool nt, uint32_t* sink,
+                   hipStream_t s) {
+  if (nt)
+    hipLaunchKernelGGL((stream_kernel<NS, ND, true>), dim3(blocks), dim3(kStreamThreads), 0, s, a,
+                       n, sink);
+  else
+    hipLaunchKernelGGL((stream_kernel<NS, ND, false>), dim3(blocks), dim3(kStreamThreads), 0, s, a,
+                       n, sink);
 }
 
 // kMfmaChains independent v_mfma_f32_32x32x16_bf16 chains per wave.
@@ -95,14 +137,6 @@ __global__ __launch_bounds__(kMfmaThreads) void exp_kernel(int iters, float* __r
   sink[(size_t)blockIdx.x * kMfmaThreads + threadIdx.x] = s;
 }
 
-int check_stream_args(const char* fn, const void* a, size_t bytes) {
-  if (!a) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
-  if (!aligned16(a)) return fail(PAB_ERR_INVALID_ARG, fmt("%s: pointers must be 16-byte aligned", fn));
-  if (bytes == 0 || bytes % 16 != 0)
-    return fail(PAB_ERR_INVALID_ARG, fmt("%s: bytes must be a positive multiple of 16", fn));
-  return PAB_OK;
-}
-
 int check_sink(const char* fn, const void* sink, size_t sink_bytes) {
   if (!sink || !aligned16(sink))
     return fail(PAB_ERR_INVALID_ARG, fmt("%s: sink NULL or not 16-byte aligned", fn));
@@ -121,25 +155,58 @@ int launched(const char* fn) {
 
 using namespace pab;
 
-extern "C" int pab_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
-  int st = check_stream_args("pab_peak_copy", src, bytes);
-  if (!st) st = check_stream_args("pab_peak_copy", dst, bytes);
-  if (st) return st;
-  if (ranges_overlap(src, bytes, dst, bytes))
-    return fail(PAB_ERR_INVALID_ARG, "pab_peak_copy: source and destination overlap");
-  hipLaunchKernelGGL(copy_kernel, dim3(kStreamBlocks), dim3(kStreamThreads), 0, (hipStream_t)stream,
-                     (const u32x4*)src, (u32x4*)dst, (int64_t)(bytes / 16));
-  return launched("pab_peak_copy");
-}
-
-extern "C" int pab_peak_read(const void* src, size_t bytes, void* sink, size_t sink_bytes,
-                             void* stream) {
-  int st = check_stream_args("pab_peak_read", src, bytes);
-  if (!st) st = check_sink("pab_peak_read", sink, sink_bytes);
-  if (st) return st;
-  hipLaunchKernelGGL(read_kernel, dim3(kStreamBlocks), dim3(kStreamThreads), 0, (hipStream_t)stream,
-                     (const u32x4*)src, (int64_t)(bytes / 16), (uint32_t*)sink);
-  return launched("pab_peak_read");
+extern "C" int pab_peak_stream(const void* const* src, int32_t n_src, void* const* dst,
+                               int32_t n_dst, size_t bytes, int32_t blocks, int32_t variant,
+                               void* sink, size_t sink_bytes, void* stream) {
+  const char* fn = "pab_peak_stream";
+  if (n_src < 0 || n_src > 4 || n_dst < 0 || n_dst > 2 || n_src + n_dst < 1)
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: need 0 <= n_src <= 4, 0 <= n_dst <= 2, one stream", fn));
+  if ((n_src && !src) || (n_dst && !dst)) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL array", fn));
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: bytes must be a positive multiple of 16", fn));
+  if (blocks < 1 || blocks > kMaxStreamBlocks)
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: blocks must be in [1, %d]", fn, kMaxStreamBlocks));
+  if (variant != 0 && variant != 1) return fail(PAB_ERR_INVALID_ARG, fmt("%s: variant is 0 or 1", fn));
+  StreamArgs a{};
+  const void* all[6];
+  size_t nall = 0;
+  for (int i = 0; i < n_src; ++i) {
+    if (!aligned16(src[i])) return fail(PAB_ERR_INVALID_ARG, fmt("%s: src[%d] NULL or misaligned", fn, i));
+    a.src[i] = (const u32x4*)src[i];
+    all[nall++] = src[i];
+  }
+  for (int i = 0; i < n_dst; ++i) {
+    if (!aligned16(dst[i])) return fail(PAB_ERR_INVALID_ARG, fmt("%s: dst[%d] NULL or misaligned", fn, i));
+    a.dst[i] = (u32x4*)dst[i];
+    all[nall++] = dst[i];
+  }
+  for (size_t i = 0; i < nall; ++i)
+    for (size_t j = i + 1; j < nall; ++j)
+      if (ranges_overlap(all[i], bytes, all[j], bytes))
+        return fail(PAB_ERR_INVALID_ARG, fmt("%s: buffers overlap", fn));
+  if (n_dst == 0) {
+    const int st = check_sink(fn, sink, sink_bytes);
+    if (st) return st;
+    if ((size_t)blocks * sizeof(uint32_t) > sink_bytes)
+      return fail(PAB_ERR_CAPACITY, fmt("%s: sink holds fewer words than blocks", fn));
+  }
+  const int64_t n = (int64_t)(bytes / 16);
+  const hipStream_t s = (hipStream_t)stream;
+  uint32_t* sk = (uint32_t*)sink;
+  const bool nt = variant == 1;
+  switch (n_src * 3 + n_dst) {
+#define PAB_MIX(ns, nd) \
+  case ns * 3 + nd:     \
+    launch_stream<ns, nd>(a, n, blocks, nt, sk, s); \
+    break;
+    PAB_MIX(0, 1) PAB_MIX(0, 2) PAB_MIX(1, 0) PAB_MIX(1, 1) PAB_MIX(1, 2) PAB_MIX(2, 0)
+    PAB_MIX(2, 1) PAB_MIX(2, 2) PAB_MIX(3, 0) PAB_MIX(3, 1) PAB_MIX(3, 2) PAB_MIX(4, 0)
+    PAB_MIX(4, 1) PAB_MIX(4, 2)
+#undef PAB_MIX
+    default:
+      return fail(PAB_ERR_INVALID_ARG, fmt("%s: unsupported stream mix", fn));
+  }
+  return launched(fn);
 }
 
 extern "C" int pab_peak_mfma_bf16(int32_t iters, void* sink, size_t sink_bytes, double* flops,
@@ -168,7 +235,7 @@ extern "C" int pab_peak_exp(int32_t iters, void* sink, size_t sink_bytes, double
 }
 
 extern "C" size_t pab_peak_sink_bytes(void) {
-  const size_t a = (size_t)kStreamBlocks * sizeof(uint32_t);
+  const size_t a = (size_t)kMaxStreamBlocks * sizeof(uint32_t);
   const size_t b = (size_t)kMfmaBlocks * kMfmaThreads * sizeof(float);
   return a > b ? a : b;
 }

@@ -51,8 +51,7 @@ EXPORTED = (
 # denominators, not part of the method.
 EXPORTED_PEAKS = (
     "pab_peak_sink_bytes",
-    "pab_peak_copy",
-    "pab_peak_read",
+    "pab_peak_stream",
     "pab_peak_mfma_bf16",
     "pab_peak_exp",
 )
@@ -160,10 +159,9 @@ def load(path: str = LIB_PATH):
     lib.pab_synth_normal.restype = C.c_int
     lib.pab_peak_sink_bytes.argtypes = []
     lib.pab_peak_sink_bytes.restype = sz
-    lib.pab_peak_copy.argtypes = [vp, vp, sz, vp]
-    lib.pab_peak_copy.restype = C.c_int
-    lib.pab_peak_read.argtypes = [vp, sz, vp, sz, vp]
-    lib.pab_peak_read.restype = C.c_int
+    lib.pab_peak_stream.argtypes = [C.POINTER(vp), i32, C.POINTER(vp), i32, sz, i32, i32, vp, sz,
+                                    vp]
+    lib.pab_peak_stream.restype = C.c_int
     for name in ("pab_peak_mfma_bf16", "pab_peak_exp"):
         fn = getattr(lib, name)
         fn.argtypes = [i32, vp, sz, C.POINTER(C.c_double), vp]
@@ -447,11 +445,25 @@ def pab_synth_normal(out, key_a: int, scale_a: float, key_b: int = 0, scale_b: f
 
 # ------------------------------------------------------------ measurement aids
 
-def measure_peaks(device=None, stream=None):
-    """Sustained peaks of this GPU from the pab_peak_* microbenchmarks, each
-    the best of a few launches timed with HIP events on ``stream``: HBM copy
-    (read + write) and read in GB/s over buffers rotated past the 256 MB
-    Infinity Cache, bf16 MFMA in TFLOP/s, v_exp_f32 in G/s."""
+# Read:write stream mixes measured by measure_peaks: name -> (sources,
+# destinations).  The attention kernels' own mixes: temporal reads Q, K, V
+# (and the previous output when it takes the attention difference) and
+# writes O; cross reads Q (and the previous output) and writes O (its text
+# K/V are negligible); the MSE reads two tensors.
+STREAM_MIXES = {"1:0": (1, 0), "0:1": (0, 1), "1:1": (1, 1), "2:1": (2, 1), "3:1": (3, 1),
+                "4:1": (4, 1), "2:0": (2, 0)}
+
+
+def measure_peaks(device=None, stream=None, stream_bytes=1 << 30):
+    """Sustained peaks of this GPU from the pab_peak_* microbenchmarks.
+
+    HBM: for every read:write mix in STREAM_MIXES, the best rate
+    ((sources + destinations) x stream_bytes per launch, 1 GiB streams by
+    default, two buffer sets used alternately) over grids of 1024 to 16384
+    blocks and plain or non-temporal accesses, each timed with HIP events
+    on ``stream``; bf16 MFMA in TFLOP/s and v_exp_f32 in G/s (best of a few
+    launches).
+    """
     import torch
 
     L = load()
@@ -459,38 +471,53 @@ def measure_peaks(device=None, stream=None):
     st = stream or torch.cuda.current_stream(dev)
     sp = C.c_void_p(st.cuda_stream)
     sink = torch.empty(int(L.pab_peak_sink_bytes()), dtype=torch.uint8, device=dev)
-    nbuf, nbytes = 4, 256 << 20
-    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2 * nbuf)]
-    for b in bufs:
-        b.fill_(1)
+    sets = [[torch.empty(stream_bytes, dtype=torch.uint8, device=dev) for _ in range(6)]
+            for _ in range(2)]
+    for bs in sets:
+        for b in bs:
+            b.fill_(1)
 
-    def best(launch, n=6):
-        ts = []
-        for i in range(n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            launch(i)
-            e1.record(st)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e-3)
-        return min(ts[1:])
+    def timed(launch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        launch()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
 
-    out = {}
-    t = best(lambda i: _check("pab_peak_copy", L.pab_peak_copy(
-        C.c_void_p(bufs[i % nbuf].data_ptr()), C.c_void_p(bufs[nbuf + i % nbuf].data_ptr()),
-        nbytes, sp)))
-    out["hbm_copy_gbs"] = 2 * nbytes / t / 1e9
-    t = best(lambda i: _check("pab_peak_read", L.pab_peak_read(
-        C.c_void_p(bufs[i % (2 * nbuf)].data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
-        sink.numel(), sp)))
-    out["hbm_read_gbs"] = nbytes / t / 1e9
+    out = {"hbm_stream_gbs": {}, "hbm_stream_best": {}, "stream_bytes": stream_bytes}
+    k = 0
+    for name, (ns, nd) in STREAM_MIXES.items():
+        best, how = None, None
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            for variant in (0, 1):
+                for rep in range(3):
+                    bs = sets[k % 2]
+                    k += 1
+                    src = (C.c_void_p * 4)(*[b.data_ptr() for b in bs[:4]])
+                    dst = (C.c_void_p * 2)(*[b.data_ptr() for b in bs[4:6]])
+                    t = timed(lambda: _check("pab_peak_stream", L.pab_peak_stream(
+                        src, ns, dst, nd, stream_bytes, blocks, variant,
+                        C.c_void_p(sink.data_ptr()), sink.numel(), sp)))
+                    if rep and (best is None or t < best):
+                        best, how = t, {"blocks": blocks, "non_temporal": bool(variant)}
+        out["hbm_stream_gbs"][name] = (ns + nd) * stream_bytes / best / 1e9
+        out["hbm_stream_best"][name] = how
+    out["hbm_read_gbs"] = out["hbm_stream_gbs"]["1:0"]
+    out["hbm_write_gbs"] = out["hbm_stream_gbs"]["0:1"]
+    out["hbm_copy_gbs"] = out["hbm_stream_gbs"]["1:1"]
+    del sets
+
+    def best_of(launch, n=6):
+        return min(timed(launch) for _ in range(n))
+
     work = C.c_double(0.0)
-    t = best(lambda i: _check("pab_peak_mfma_bf16", L.pab_peak_mfma_bf16(
+    t = best_of(lambda: _check("pab_peak_mfma_bf16", L.pab_peak_mfma_bf16(
         2048, C.c_void_p(sink.data_ptr()), sink.numel(), C.byref(work), sp)))
     out["mfma_bf16_tflops"] = work.value / t / 1e12
-    t = best(lambda i: _check("pab_peak_exp", L.pab_peak_exp(
+    t = best_of(lambda: _check("pab_peak_exp", L.pab_peak_exp(
         2048, C.c_void_p(sink.data_ptr()), sink.numel(), C.byref(work), sp)))
     out["exp_gps"] = work.value / t / 1e9
-    del bufs, sink
+    del sink
     torch.cuda.empty_cache()
     return out

@@ -44,15 +44,28 @@ def test_exports_every_declared_symbol():
 def test_peak_helpers_validate_before_launch():
     L = lib.load()
     sink_bytes = int(L.pab_peak_sink_bytes())
-    assert sink_bytes >= 8192 * 4
+    assert sink_bytes >= 65536 * 4
     work = C.c_double(0.0)
-    assert L.pab_peak_copy(None, C.c_void_p(0x1000), 1024, None) == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_peak_copy(C.c_void_p(0x1000), C.c_void_p(0x1008), 1024, None) == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_peak_copy(C.c_void_p(0x1000), C.c_void_p(0x1200), 1024, None) == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_peak_read(C.c_void_p(0x1000), 1000, C.c_void_p(0x100000), sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_peak_read(C.c_void_p(0x1000), 1024, C.c_void_p(0x100000), 16, None) == lib.PAB_ERR_CAPACITY
-    assert L.pab_peak_mfma_bf16(0, C.c_void_p(0x100000), sink_bytes, C.byref(work), None) == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_peak_exp(1, C.c_void_p(0x100000), 64, C.byref(work), None) == lib.PAB_ERR_CAPACITY
+    P = lambda *a: (C.c_void_p * len(a))(*[C.c_void_p(x) for x in a])
+    sink = C.c_void_p(0x100000)
+    src, dst = P(0x1000, 0x100000000), P(0x200000000)
+    # no stream / too many streams
+    assert L.pab_peak_stream(src, 0, dst, 0, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(src, 5, dst, 0, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(src, 1, dst, 3, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    # size, grid, variant
+    assert L.pab_peak_stream(src, 1, dst, 1, 1000, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(src, 1, dst, 1, 1024, 0, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(src, 1, dst, 1, 1024, 70000, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(src, 1, dst, 1, 1024, 1024, 2, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    # misaligned and overlapping buffers
+    assert L.pab_peak_stream(P(0x1008), 1, dst, 1, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(P(0x1000), 1, P(0x1200), 1, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_stream(P(0x1000, 0x1100), 2, dst, 0, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    # a read-only pass needs a sink of pab_peak_sink_bytes()
+    assert L.pab_peak_stream(src, 1, dst, 0, 1024, 1024, 0, sink, 16, None) == lib.PAB_ERR_CAPACITY
+    assert L.pab_peak_mfma_bf16(0, sink, sink_bytes, C.byref(work), None) == lib.PAB_ERR_INVALID_ARG
+    assert L.pab_peak_exp(1, sink, 64, C.byref(work), None) == lib.PAB_ERR_CAPACITY
 
 
 @pytest.mark.parametrize("win", [(15, 85), (0, 100), (50, 50), (0, 0), (30, 60), (10, 90)])

@@ -77,35 +77,56 @@ def _sample_check(cfg, kind, q, k, v, out, label):
 
 
 def _run_checked(cfg, pab=True, blocks_checked=(0,), check_steps=None, resident=True,
-                 max_steps=None):
+                 max_steps=None, print_blocks=None, reuse_check_steps=()):
+    """Run a trajectory and check it as it goes.
+
+    Every step: the dispatch mask equals the oracle schedule (all blocks).
+    Every recompute of a block in ``print_blocks`` (default: the checked
+    blocks) records a bit fingerprint of the slot; every reuse step of such a
+    block must hand back the source step's slot with the same fingerprint.
+    At ``check_steps`` the recomputed outputs of ``blocks_checked`` are
+    compared with the oracle (sampled rows); at ``reuse_check_steps`` the
+    reused outputs are compared with the oracle on the source step's inputs
+    (drawn again from their generator counters).
+    """
     dev = torch.device("cuda:0")
     traj = harness.Trajectory(cfg, pab=pab, device=dev)
     need = traj.steps_needed()
     if max_steps is not None:
         need = [x for x in need if x[2] < max_steps]
-    traj.inputs = harness.Inputs(cfg, need, device=dev, resident=resident)
+    traj.inputs = harness.Inputs(cfg, need if resident else [], device=dev, resident=resident)
     ranges = list(cfg.ranges) if pab else [0] * len(cfg.kinds)
     rec, src, cnt = oracle.schedule(cfg.N, ranges)
     assert np.array_equal(traj.recompute, rec) and np.array_equal(traj.counts, cnt)
     prints = {}
     w0 = -(-15 * cfg.N // 100)
     check_steps = set(check_steps if check_steps is not None else (0, w0, cfg.N - 1))
+    print_blocks = tuple(blocks_checked if print_blocks is None else print_blocks)
+    reuse_seen = {"n": 0, "oracle": 0}
 
     def on_step(i, outs):
         torch.cuda.synchronize()
-        for b in blocks_checked:
+        for b in sorted(set(print_blocks) | set(blocks_checked)):
             for a, kind in enumerate(cfg.kinds):
                 ptr = outs[b][i][a]
                 slot = traj.slot_tensor(b, a, ptr)
                 j = int(src[i, a])
                 if j == i:
-                    prints[(b, a, i)] = _fingerprint(slot)
-                    if i in check_steps:
+                    if b in print_blocks:
+                        prints[(b, a, i)] = _fingerprint(slot)
+                    if b in blocks_checked and i in check_steps:
                         q, k, v = traj.inputs.get(b, a, i)
                         _sample_check(cfg, kind, q, k, v, slot, f"{cfg.name} b{b} {kind} step {i}")
                 else:
                     assert ptr == outs[b][j][a], "reuse must hand back the source slot"
-                    assert _fingerprint(slot) == prints[(b, a, j)], "reused bytes changed"
+                    if b in print_blocks:
+                        assert _fingerprint(slot) == prints[(b, a, j)], "reused bytes changed"
+                        reuse_seen["n"] += 1
+                    if b in blocks_checked and i in reuse_check_steps:
+                        q, k, v = traj.inputs.get(b, a, j)
+                        _sample_check(cfg, kind, q, k, v, slot,
+                                      f"{cfg.name} b{b} {kind} step {i} (reuses {j})")
+                        reuse_seen["oracle"] += 1
 
     res = traj.run(on_step=on_step, max_steps=max_steps)
     n = cfg.N if max_steps is None else max_steps
@@ -113,13 +134,18 @@ def _run_checked(cfg, pab=True, blocks_checked=(0,), check_steps=None, resident=
         for i in range(n):
             for a in range(len(cfg.kinds)):
                 assert ((int(res["masks"][b, i]) >> a) & 1) == rec[i, a]
+    # every reuse of a fingerprinted block was checked
+    n_reuse = sum(1 for i in range(n) for a in range(len(cfg.kinds)) if not rec[i, a])
+    assert reuse_seen["n"] == n_reuse * len(print_blocks)
+    if reuse_check_steps:
+        assert reuse_seen["oracle"] > 0
     return traj, res
 
 
 def test_tiny_trajectory_every_step():
     _need_gpu()
     cfg = harness.CONFIGS["tiny"]
-    _run_checked(cfg, check_steps=range(cfg.N))
+    _run_checked(cfg, check_steps=range(cfg.N), reuse_check_steps=range(cfg.N))
 
 
 def test_tiny_trajectory_pab_off():
@@ -131,12 +157,21 @@ def test_tiny_trajectory_pab_off():
 
 def test_b480_trajectory():
     _need_gpu()
-    _run_checked(harness.CONFIGS["b480"])
+    _run_checked(harness.CONFIGS["b480"], reuse_check_steps=(6,))
+
+
+def test_b720_trajectory():
+    # 3600-token frames: recomputes checked at the first step, the window's
+    # first step and the last step, a broadcast step against its source.
+    _need_gpu()
+    _run_checked(harness.CONFIGS["b720"], resident=False, reuse_check_steps=(7,))
 
 
 def test_full3d_trajectory():
+    # Window 8..42 (N = 50); step 9 reuses step 8 for both types.
     _need_gpu()
-    _run_checked(harness.CONFIGS["full3d"], check_steps=(8,))
+    _run_checked(harness.CONFIGS["full3d"], resident=False, check_steps=(0, 8, 49),
+                 reuse_check_steps=(9,))
 
 
 def test_cfg480_padded_prompts_trajectory():
@@ -146,12 +181,18 @@ def test_cfg480_padded_prompts_trajectory():
     _run_checked(harness.CONFIGS["cfg480"])
 
 
-def test_stack28_cache_first_steps():
-    # 28 blocks x 3 types x 2 slots resident in HBM; the first 8 steps cover
-    # the outer steps, the window entry (step 5) and broadcast steps 6, 7.
+def test_stack28_trajectory():
+    # The whole 30-step trajectory of the 28-block stack: 28 x 3 x 2 cache
+    # slots resident in HBM (29.5 GB), inputs drawn per recompute.  The
+    # dispatch mask is checked for every (block, step); every block's reused
+    # outputs are the source slots with unchanged bytes through the whole
+    # window; blocks 0, 13 and 27 are compared with the oracle at the first
+    # step, the window's first step (5), a broadcast step (6, which reuses
+    # step 5 for all three types) and the last step (29).
     _need_gpu()
     cfg = harness.CONFIGS["stack28"]
-    _run_checked(cfg, blocks_checked=(0, 13, 27), check_steps=(5,), resident=False, max_steps=8)
+    _run_checked(cfg, blocks_checked=(0, 13, 27), check_steps=(0, 5, 29), resident=False,
+                 print_blocks=range(cfg.blocks), reuse_check_steps=(6,))
 
 
 # Shapes of the drift test: each reaches a different way the dispatcher takes
