@@ -29,14 +29,15 @@ size_t pab_peak_sink_bytes(void);
  * n_dst = 0 the XOR is folded into one word per block written to sink.
  * Moves (n_src + n_dst) * bytes through HBM when no buffer is cache
  * resident (use buffers much larger than the 256 MB Infinity Cache, or
- * rotate).  A grid-stride loop over `blocks` blocks of 256 threads keeps
- * four vectors of every stream in flight per thread; variant 0 uses plain
- * loads and stores, 1 non-temporal ones.  The caller picks the best grid
- * and variant for each read/write mix.
+ * rotate).  `blocks` blocks of 256 threads; `variant` selects the access
+ * pattern: bit 0 = non-temporal loads and stores; bits 1-2 = vectors of
+ * every stream in flight per thread (0: 4, 1: 8, 2: 16); bit 3 = each block
+ * walks one contiguous chunk (else a grid-stride loop over the buffers).
+ * The caller picks the best grid and variant for each read/write mix.
  * Errors: PAB_ERR_INVALID_ARG for n_src outside [0, 4], n_dst outside
  *   [0, 2], no stream, NULL/misaligned/overlapping buffers, bytes not a
- *   positive multiple of 16, blocks outside [1, 65536] or a variant other
- *   than 0 or 1; PAB_ERR_CAPACITY for a sink (n_dst = 0) smaller than
+ *   positive multiple of 16, blocks outside [1, 65536] or an unknown
+ *   variant; PAB_ERR_CAPACITY for a sink (n_dst = 0) smaller than
  *   pab_peak_sink_bytes() or than `blocks` words.
  */
 int pab_peak_stream(const void* const* src, int32_t n_src, void* const* dst, int32_t n_dst,

@@ -55,7 +55,8 @@ FLAGS = [
 
 # Per-source extra flags.  The spatial kernel's row maxima see no NaN (scores
 # of finite inputs, masked entries are -inf), so its max needs no NaN
-# quieting: this drops a canonicalizing VALU op per max chain.
+# quieting: this drops a canonicalizing VALU op per max chain.  (Its finite
+# tests read exponent bits, which this flag leaves alone.)
 EXTRA = {
     "spatial.hip": ["-fno-honor-nans"],
 }

@@ -16,7 +16,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStreamThreads = 256;
 constexpr int kMaxStreamBlocks = 65536;
-constexpr int kUnroll = 4;
 constexpr int kMfmaBlocks = 2048;     // 4-wave blocks: 32 waves per CU on 256 CUs
 constexpr int kMfmaThreads = 256;
 constexpr int kMfmaChains = 4;        // independent accumulators per wave
@@ -34,49 +33,67 @@ __device__ __forceinline__ void st(u32x4* p, u32x4 v, bool nt) {
 struct StreamArgs {
   const u32x4* src[4];
   u32x4* dst[2];
+  int ns, nd;
 };
 
-// One pass over n 16-byte vectors of NS source and ND destination streams:
-// dst_j[i] = XOR over the sources of src[i] (or i itself with no source);
-// with no destination the XOR is folded into one word per block.  A
-// grid-stride loop with kUnroll vectors of every stream in flight per
-// thread; whole-vector tails run one vector at a time.
-template <int NS, int ND, bool NT>
+// One pass over n 16-byte vectors of a.ns source and a.nd destination
+// streams: dst_j[i] = XOR over the sources of src[i] (or i itself with no
+// source); with no destination the XOR is folded into one word per block.
+// Each thread keeps U vectors of every stream in flight.  Layout: CH = false
+// strides the whole grid over the buffers (a wave's U vectors are a grid
+// apart); CH = true gives every block one contiguous chunk, walked U x 4 KiB
+// at a time.  Tails run one vector at a time.
+template <bool NT, int U, bool CH>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(StreamArgs a, int64_t n,
                                                               uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-  int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  int64_t i, stride, end, ustep;
+  if (CH) {
+    const int64_t per = ((n + gridDim.x - 1) / gridDim.x + kStreamThreads - 1) / kStreamThreads *
+                        kStreamThreads;
+    i = (int64_t)blockIdx.x * per + threadIdx.x;
+    end = (int64_t)(blockIdx.x + 1) * per;
+    end = end < n ? end : n;
+    ustep = kStreamThreads;
+    stride = (int64_t)U * kStreamThreads;
+  } else {
+    i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    end = n;
+    ustep = (int64_t)gridDim.x * kStreamThreads;
+    stride = (int64_t)U * ustep;
+  }
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-    u32x4 v[kUnroll];
+  for (; i + (U - 1) * ustep < end; i += stride) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t w = (uint32_t)(i + u * stride);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w = (uint32_t)(i + u * ustep);
       v[u] = u32x4{w, w, w, w};
     }
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < 4; ++s)
+      if (s < a.ns) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] ^= ld(a.src[s] + i + u * stride, NT);
+        for (int u = 0; u < U; ++u) v[u] ^= ld(a.src[s] + i + u * ustep, NT);
+      }
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+    for (int d = 0; d < 2; ++d)
+      if (d < a.nd) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) st(a.dst[d] + i + u * stride, v[u], NT);
-    if (ND == 0) {
+        for (int u = 0; u < U; ++u) st(a.dst[d] + i + u * ustep, v[u], NT);
+      }
+    if (a.nd == 0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+      for (int u = 0; u < U; ++u) acc ^= v[u];
     }
   }
-  for (; i < n; i += stride) {
+  for (; i < end; i += ustep) {
     const uint32_t w = (uint32_t)i;
     u32x4 v = {w, w, w, w};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) v ^= a.src[s][i];
-#pragma unroll
-    for (int d = 0; d < ND; ++d) a.dst[d][i] = v;
-    if (ND == 0) acc ^= v;
+    for (int s = 0; s < a.ns; ++s) v ^= a.src[s][i];
+    for (int d = 0; d < a.nd; ++d) a.dst[d][i] = v;
+    acc ^= v;
   }
-  if (ND == 0) {
+  if (a.nd == 0) {
     __shared__ uint32_t red[kStreamThreads];
     red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
     __syncthreads();
@@ -88,15 +105,26 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(StreamArgs a, in
   }
 }
 
-template <int NS, int ND>
-void launch_stream(const StreamArgs& a, int64_t n, int blocks, bool nt, uint32_t* sink,
-                   hipStream_t s) {
-  if (nt)
-    hipLaunchKernelGGL((stream_kernel<NS, ND, true>), dim3(blocks), dim3(kStreamThreads), 0, s, a,
-                       n, sink);
+template <bool NT, int U>
+void launch_stream_u(const StreamArgs& a, int64_t n, int blocks, bool ch, uint32_t* sink,
+                     hipStream_t s) {
+  if (ch)
+    hipLaunchKernelGGL((stream_kernel<NT, U, true>), dim3(blocks), dim3(kStreamThreads), 0, s, a, n,
+                       sink);
   else
-    hipLaunchKernelGGL((stream_kernel<NS, ND, false>), dim3(blocks), dim3(kStreamThreads), 0, s, a,
-                       n, sink);
+    hipLaunchKernelGGL((stream_kernel<NT, U, false>), dim3(blocks), dim3(kStreamThreads), 0, s, a, n,
+                       sink);
+}
+
+template <bool NT>
+void launch_stream_nt(const StreamArgs& a, int64_t n, int blocks, int u, bool ch, uint32_t* sink,
+                      hipStream_t s) {
+  if (u == 0)
+    launch_stream_u<NT, 4>(a, n, blocks, ch, sink, s);
+  else if (u == 1)
+    launch_stream_u<NT, 8>(a, n, blocks, ch, sink, s);
+  else
+    launch_stream_u<NT, 16>(a, n, blocks, ch, sink, s);
 }
 
 // kMfmaChains independent v_mfma_f32_32x32x16_bf16 chains per wave.
@@ -166,8 +194,11 @@ extern "C" int pab_peak_stream(const void* const* src, int32_t n_src, void* cons
     return fail(PAB_ERR_INVALID_ARG, fmt("%s: bytes must be a positive multiple of 16", fn));
   if (blocks < 1 || blocks > kMaxStreamBlocks)
     return fail(PAB_ERR_INVALID_ARG, fmt("%s: blocks must be in [1, %d]", fn, kMaxStreamBlocks));
-  if (variant != 0 && variant != 1) return fail(PAB_ERR_INVALID_ARG, fmt("%s: variant is 0 or 1", fn));
+  if (variant < 0 || variant > 15 || ((variant >> 1) & 3) == 3)
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: unknown variant %d", fn, variant));
   StreamArgs a{};
+  a.ns = n_src;
+  a.nd = n_dst;
   const void* all[6];
   size_t nall = 0;
   for (int i = 0; i < n_src; ++i) {
@@ -193,19 +224,12 @@ extern "C" int pab_peak_stream(const void* const* src, int32_t n_src, void* cons
   const int64_t n = (int64_t)(bytes / 16);
   const hipStream_t s = (hipStream_t)stream;
   uint32_t* sk = (uint32_t*)sink;
-  const bool nt = variant == 1;
-  switch (n_src * 3 + n_dst) {
-#define PAB_MIX(ns, nd) \
-  case ns * 3 + nd:     \
-    launch_stream<ns, nd>(a, n, blocks, nt, sk, s); \
-    break;
-    PAB_MIX(0, 1) PAB_MIX(0, 2) PAB_MIX(1, 0) PAB_MIX(1, 1) PAB_MIX(1, 2) PAB_MIX(2, 0)
-    PAB_MIX(2, 1) PAB_MIX(2, 2) PAB_MIX(3, 0) PAB_MIX(3, 1) PAB_MIX(3, 2) PAB_MIX(4, 0)
-    PAB_MIX(4, 1) PAB_MIX(4, 2)
-#undef PAB_MIX
-    default:
-      return fail(PAB_ERR_INVALID_ARG, fmt("%s: unsupported stream mix", fn));
-  }
+  const int u = (variant >> 1) & 3;
+  const bool ch = (variant >> 3) & 1;
+  if (variant & 1)
+    launch_stream_nt<true>(a, n, blocks, u, ch, sk, s);
+  else
+    launch_stream_nt<false>(a, n, blocks, u, ch, sk, s);
   return launched(fn);
 }
 

@@ -11,21 +11,27 @@
 // block instead, so fewer of its waves sit idle.  Keys arrive
 // in 64-row tiles through an LDS ring filled by direct global->LDS loads
 // (global_load_lds_dwordx4): each tile is a whole number of 1 KiB wave-wide
-// loads, dealt round-robin to the waves, issued two tiles ahead (four-stage
-// ring; three stages and one tile ahead where four would not leave room for
-// two blocks per CU).  No registers are spent on staging.
+// loads, dealt round-robin to the waves (every wave issues the same number;
+// a wave short of a load repeats one, writing the same bytes), issued two
+// tiles ahead (four-stage ring; three stages and one tile ahead where four
+// would not leave room for two blocks per CU).  No registers are spent on
+// staging.
 //
 // Each wave walks its keys in 32-key units and software-pipelines them so the
 // matrix cores and the vector ALUs work at the same time: while the softmax of
 // unit u (exponentials, bf16 packing) runs on the VALU, the MFMAs compute the
-// scores of unit u+1 and then O^T += V^T P^T for unit u; the row maxima of
-// unit u+1 are taken under the last of those MFMAs.
+// scores of unit u+1 and then O^T += V^T P^T for unit u.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of
-//     ONE query row, so row statistics need one exchange with the other
-//     half-wave;
-//   * online softmax with a lazy running max: the max is only raised when a
-//     unit's max exceeds it by more than 8 (log2 units); p <= 2^8 and
-//     rescales become rare after the first units;
+//     ONE query row;
+//   * the softmax needs no running maximum.  Softmax is unchanged by the
+//     constant subtracted from a row's scores; it only has to keep exp() in
+//     range.  Each row takes the maximum of its first 32 scores, plus 16
+//     (log2 units) of headroom, and keeps it: every p = 2^(s c - m) then
+//     stays finite unless a later score exceeds that first maximum by more
+//     than about 100 (log2 units), far outside ordinary inputs.  The hot
+//     loop thus holds no maximum, no rescale and no branch.  A wave whose
+//     denominators or outputs come out non-finite (the rare case) recomputes
+//     its rows exactly: a two-pass fp32 softmax per row, straight from HBM;
 //   * O^T += V^T P^T: the V^T operand comes straight from the row-major V
 //     tile through ds_read_b64_tr_b16 (transposing LDS read).  Operand row D
 //     (a padding row of the last 32-row block) is set to ones, so O^T row D
@@ -50,7 +56,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kBN = 64;                  // keys per LDS tile
 constexpr int kLds = 160 * 1024;         // LDS bytes per CU
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSlack = 8.0f;           // lazy-rescale threshold (log2 units)
+constexpr float kHeadroom = 16.0f;       // reference max above the first unit's (log2 units)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -95,7 +101,7 @@ struct Geo {
   static constexpr int KREG = kBN * KS;             // elements
   static constexpr int VREG = kBN * VS;
   static constexpr int NJ = KCH + VCH;
-  static constexpr int NJW = (NJ + kWaves - 1) / kWaves;  // loads per wave per tile, at most
+  static constexpr int NJW = (NJ + kWaves - 1) / kWaves;  // loads per wave per tile
   // Transposing reads of V past the last data column (operand rows > D, whose
   // products are discarded) may run past the V rows into this slack.
   static constexpr int VSLACK = 64;
@@ -152,6 +158,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Finite test on the exponent bits (the file is compiled assuming no NaN,
+// which would let a floating-point test fold away).
+__device__ __forceinline__ bool finite(float x) {
+  return (__builtin_bit_cast(uint32_t, x) & 0x7F800000u) != 0x7F800000u;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const bf16* __restrict__ Q,
                                                              const bf16* __restrict__ K,
@@ -179,59 +191,61 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
   const bf16* __restrict__ Ps = P ? P + base : nullptr;
   double dsum = 0.0;
 
-  // Direct-load plan of this wave: loads j = wave + 4i.  Load j covers stage
-  // slots 64 j .. 64 j + 63; slot s of the K (V) rows is chunk
+  // Direct-load plan of this wave: loads j = wave + 4i; a wave whose last
+  // j is past the tile repeats load j - NJ instead (the same bytes to the
+  // same place), so every wave issues NJW loads per tile.  Load j covers
+  // stage slots 64 j .. 64 j + 63; slot s of the K (V) rows is chunk
   // (row, ch) = (s / KCH, s % KCH) (V: VCH).  Pad chunks (ch >= D/8) re-read
   // chunk 0 of the tile: finite values that nothing uses.  Byte offsets are
   // relative to the tile's first row.
-  uint32_t joff[G::NJW];
-#pragma unroll
-  for (int i = 0; i < G::NJW; ++i) {
-    const int j = wave + kWaves * i;
+  auto load_j = [&](int i) {  // wave-uniform
+    const int j0 = wave + kWaves * i;
+    return j0 < G::NJ ? j0 : j0 - G::NJ;
+  };
+  auto load_slot = [&](int j, int& row, int& ch) {
     const bool is_k = j < G::KCH;
     const int cs = is_k ? G::KCH : G::VCH;
     const int s = (is_k ? j : j - G::KCH) * kWave + lane;
-    const int row = s / cs, ch = s % cs;
-    joff[i] = (j < G::NJ && ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
+    row = s / cs;
+    ch = s % cs;
+  };
+  uint32_t joff[G::NJW];
+#pragma unroll
+  for (int i = 0; i < G::NJW; ++i) {
+    int row, ch;
+    load_slot(load_j(i), row, ch);
+    joff[i] = (ch < G::DCH) ? (uint32_t)((row * D + ch * 8) * 2) : 0u;
   }
-  const int nj_wave = (G::NJ - wave + kWaves - 1) / kWaves;  // loads this wave issues per tile
   const uint32_t ring_lds = (uint32_t)(uintptr_t)LDS_PTR(void, ring);
   const int nt = (S + kBN - 1) / kBN;
   auto stage_base = [&](int t) -> uint32_t {
     return ring_lds + (uint32_t)((t % G::NST) * G::STAGE * 2);
   };
-  auto issue = [&](int t) {
+  auto issue = [&](int t, auto full_known) {
     const int key0 = t * kBN;
     const uint32_t st = stage_base(t);
-    if (key0 + kBN <= S) {
+    if (decltype(full_known)::value || key0 + kBN <= S) {
       const bf16* kt = Ks + (size_t)key0 * D;
       const bf16* vt = Vs + (size_t)key0 * D;
 #pragma unroll
       for (int i = 0; i < G::NJW; ++i) {
-        const int j = wave + kWaves * i;
-        if (i + 1 < G::NJW || j < G::NJ) dma16(j < G::KCH ? kt : vt, joff[i], st + (uint32_t)(j * 1024));
+        const int j = load_j(i);
+        dma16(j < G::KCH ? kt : vt, joff[i], st + (uint32_t)(j * 1024));
       }
     } else {
       // Ragged last tile: rows past S repeat row S-1 (finite; their scores
       // are masked and their p are 0).
 #pragma unroll
       for (int i = 0; i < G::NJW; ++i) {
-        const int j = wave + kWaves * i;
-        if (i + 1 < G::NJW || j < G::NJ) {
-          const bool is_k = j < G::KCH;
-          const int cs = is_k ? G::KCH : G::VCH;
-          const int s = (is_k ? j : j - G::KCH) * kWave + lane;
-          const int row = s / cs, ch = s % cs;
-          const int r = min(key0 + row, S - 1);
-          const uint32_t off = (ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
-          dma16(is_k ? Ks : Vs, off, st + (uint32_t)(j * 1024));
-        }
+        const int j = load_j(i);
+        int row, ch;
+        load_slot(j, row, ch);
+        const int r = min(key0 + row, S - 1);
+        const uint32_t off = (ch < G::DCH) ? (uint32_t)((r * D + ch * 8) * 2) : 0u;
+        dma16(j < G::KCH ? Ks : Vs, off, st + (uint32_t)(j * 1024));
       }
     }
   };
-  // Barrier B_t: tile t has landed and is visible to every wave; the stage
-  // read last by unit 2t-3 is free again and is refilled with the tile
-  // NST-2 ahead.
   // The previous output P (attention difference) with a four-stage ring:
   // once the last tile is synchronized, stages nt and nt+1 (mod 4) are
   // never refilled and every wave is done reading them (the scores taken
@@ -260,18 +274,23 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
       if (pos < bytes) dma16(pb, min(pos, valid - 16u), dst + j * 1024);
     }
   };
-  auto sync_tile = [&](int t) {
-    if (G::NST == 4 && t + 1 < nt) {  // tile t+1 may still be in flight
-      if (nj_wave == G::NJW) {
-        wait_vmcnt<G::NJW>();
-      } else {
-        wait_vmcnt<(G::NJW > 1 ? G::NJW - 1 : 0)>();
-      }
+  // Barrier B_t: tile t has landed and is visible to every wave; the stage
+  // read last by unit 2t-3 is free again and is refilled with the tile
+  // NST-2 ahead.  `steady`: that tile is known to exist and to be whole (so
+  // is tile t+1), which the main loop guarantees; else both are checked.
+  auto sync_tile = [&](int t, auto steady) {
+    constexpr bool kSteady = decltype(steady)::value;
+    if (G::NST == 4 && (kSteady || t + 1 < nt)) {  // tile t+1 may still be in flight
+      wait_vmcnt<G::NJW>();
     } else {
       wait_vmcnt<0>();
     }
     __syncthreads();
-    if (t + G::NST - 2 < nt) issue(t + G::NST - 2);
+    if constexpr (kSteady) {
+      issue(t + G::NST - 2, std::true_type{});
+    } else {
+      if (t + G::NST - 2 < nt) issue(t + G::NST - 2, std::false_type{});
+    }
   };
 
   // The work of one block for QBX 32-row query blocks per wave.
@@ -299,12 +318,12 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
     // at the first use of Q inside the loop.
     wait_vmcnt<0>();
 
-    issue(0);
-    if (G::NST == 4 && nt > 1) issue(1);
+    issue(0, std::false_type{});
+    if (G::NST == 4 && nt > 1) issue(1, std::false_type{});
 
     if (!wave_live) {
       // Idle waves still fetch their share of every tile.
-      for (int t = 0; t < nt; ++t) sync_tile(t);
+      for (int t = 0; t < nt; ++t) sync_tile(t, std::false_type{});
       return;
     }
 
@@ -325,9 +344,7 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
     for (int qb = 0; qb < QBX; ++qb)
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb) oacc[qb][nb] = zero16();
-    float mrow[QBX];
-#pragma unroll
-    for (int qb = 0; qb < QBX; ++qb) mrow[qb] = -INFINITY;  // log2 domain (score * c)
+    float mrow[QBX];  // reference max per row (log2 domain, score * c), fixed
 
     // S^T block of the 32 keys at row kb*32 of the stage whose K rows `kaddr`
     // points into (per-lane offset included).
@@ -348,31 +365,6 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (key_first + acc_row(r, h) >= S) s[qb][r] = -INFINITY;
-    };
-    auto rowmax = [&](const f32x16 (&s)[QBX], float (&mx)[QBX]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int qb = 0; qb < QBX; ++qb) {
-        float m = s[qb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][r]);
-        mx[qb] = max_halves(m);
-      }
-    };
-    // Raise the running max where a unit's max exceeds it by more than the
-    // slack, rescaling what has been accumulated so far.
-    auto rescale = [&](const float (&mx)[QBX]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int qb = 0; qb < QBX; ++qb) {
-        const float mnew = mx[qb] * c;
-        if (mnew > mrow[qb] + kSlack) {
-          const float alpha = fast_exp2(mrow[qb] - mnew);
-#pragma unroll
-          for (int nb = 0; nb < G::NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
-          mrow[qb] = mnew;
-        }
-      }
     };
     // P^T operand (bf16) of scores r0..r0+7 (r0 = 8*t2): 16 keys per lane half.
     auto probs = [&](const f32x16 (&s)[QBX], int t2, bf16x8 (&pb)[QBX]) __attribute__((always_inline)) {
@@ -415,12 +407,10 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
     };
     // One pipelined unit: softmax and PV of the current unit (scores `sc`, V at
     // row kb_cur*32 of `v_cur`) around the QK of the next unit (K at row
-    // kb_next*32 of `k_next`, scores into `sn`, row maxima into `mxn`).  The
-    // MFMA and VALU streams sit in one basic block, so the scheduler can
-    // interleave them.  With `masked`, keys of the next unit from S on are
-    // masked (only the last tile has such keys).
+    // kb_next*32 of `k_next`, scores into `sn`).  With `masked`, keys of the
+    // next unit from S on are masked (only the last tile has such keys).
     auto unit = [&](auto masked, uint32_t k_next, int kb_next, int key_next, uint32_t v_cur,
-                    int kb_cur, const f32x16 (&sc)[QBX], f32x16 (&sn)[QBX], float (&mxn)[QBX])
+                    int kb_cur, const f32x16 (&sc)[QBX], f32x16 (&sn)[QBX])
         __attribute__((always_inline)) {
       bf16x8 p0[QBX], p1[QBX];
       qk(k_next, kb_next, sn);
@@ -429,42 +419,49 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
       probs(sc, 1, p1);
       pv(v_cur, kb_cur, 1, p1);
       if constexpr (decltype(masked)::value) mask(sn, key_next);
-      rowmax(sn, mxn);
     };
 
     f32x16 sA[QBX], sB[QBX];
-    float mA[QBX], mB[QBX];
 
-    sync_tile(0);
+    sync_tile(0, std::false_type{});
     {
       const uint32_t st = stage_base(0);
       qk(opaque(st + klane), 0, sA);
       if (S < 32) mask(sA, 0);
-      rowmax(sA, mA);
+      // Reference max: the first unit's row max (the other half-wave holds
+      // the other 16 keys of the row), plus headroom.
+#pragma unroll
+      for (int qb = 0; qb < QBX; ++qb) {
+        float m = sA[qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, sA[qb][r]);
+        mrow[qb] = max_halves(m) * c + kHeadroom;
+      }
     }
 
     // One tile per iteration: units 2t (scores in sA) and 2t+1, each with the
     // QK of the unit after it underneath.  While both of those units have all
-    // 32 keys below S the iteration needs no masking.
+    // 32 keys below S the iteration needs no masking; while the tile NST-2
+    // ahead of the next is whole, its loads need no check either and the
+    // iteration is one basic block.
     const int UF = S / 32;   // units with all 32 keys present
     int t = 0;
-    for (; 2 * t + 2 < UF; ++t) {
+    auto tile = [&](auto steady) __attribute__((always_inline)) {
       const uint32_t cur = stage_base(t);
       const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
-      rescale(mA);
-      unit(std::false_type{}, kc, 1, 0, vc, 0, sA, sB, mB);
-      rescale(mB);
-      sync_tile(t + 1);
+      unit(std::false_type{}, kc, 1, 0, vc, 0, sA, sB);
+      sync_tile(t + 1, steady);
       const uint32_t kn = opaque(stage_base(t + 1) + klane);
-      unit(std::false_type{}, kn, 0, 0, vc, 1, sB, sA, mA);
-    }
-    // The last one or two tiles, masked.  A unit entirely past S (the second
-    // unit of the last tile when S % 64 is 1..32) has all p exactly 0 and
-    // changes nothing; the QK after the last unit runs on stale but in-bounds
-    // LDS and is dropped.
-    // The previous output (attention difference) is fetched once the last
-    // tile is synchronized: here, in the last one or two tiles, so the hot
-    // loop above carries none of it.
+      unit(std::false_type{}, kn, 0, 0, vc, 1, sB, sA);
+    };
+    for (; 2 * t + 2 < UF && (t + G::NST) * kBN <= S; ++t) tile(std::true_type{});
+    for (; 2 * t + 2 < UF; ++t) tile(std::false_type{});
+    // The last tiles, masked.  A unit entirely past S (the second unit of the
+    // last tile when S % 64 is 1..32) has all p exactly 0 and changes
+    // nothing; the QK after the last unit runs on stale but in-bounds LDS and
+    // is dropped.  The previous output (attention difference) is fetched
+    // once the last tile is synchronized: here, in the last one or two
+    // tiles, so the hot loop above carries none of it.
     const int t_tail = t;
     for (; t < nt; ++t) {
       if constexpr (G::NST == 4) {
@@ -472,30 +469,96 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
       }
       const uint32_t cur = stage_base(t);
       const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
-      rescale(mA);
-      unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB, mB);
-      rescale(mB);
+      unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB);
       if (t + 1 < nt) {
-        sync_tile(t + 1);
+        sync_tile(t + 1, std::false_type{});
         if constexpr (G::NST == 4) {
           if (Ps && t + 1 == nt - 1) issue_prev();
         }
       }
       const uint32_t kn = opaque(stage_base(t + 1) + klane);
-      unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA, mA);
+      unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA);
     }
 
-    // The output rows, normalized by the denominator in row D of O^T.
-    auto out_word = [&](int qb, int nb, int g, float inv) __attribute__((always_inline)) {
-      return make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * inv, oacc[qb][nb][g * 4 + 1] * inv),
-                        pack_bf16x2(oacc[qb][nb][g * 4 + 2] * inv, oacc[qb][nb][g * 4 + 3] * inv));
-    };
+    // Denominators (row D of O^T) and the check that the reference max kept
+    // every value finite: data rows and the denominator of every row of the
+    // wave.  Otherwise the whole wave's rows are recomputed exactly below.
     float inv[QBX];
+    bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QBX; ++qb) {
       const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
-      inv[qb] = 1.f / (G::HD == 0 ? pr.lo : pr.hi);
+      const float l = G::HD == 0 ? pr.lo : pr.hi;
+      bad |= !(finite(l) && l > 0.f);
+      inv[qb] = 1.f / l;
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (nb * 32 + acc_row(r, 0) < D) bad |= !finite(oacc[qb][nb][r]);
     }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      // Exact recompute of this wave's rows, one row per lane: two passes
+      // over the keys in HBM (row max, then the weighted sums) in fp32.
+      if constexpr (G::NST == 4) {
+        wait_vmcnt<0>();  // the previous output's loads into the ring are done
+      }
+      const int row = qrow0 + lane;
+      if (lane < 32 * QBX && row < S) {
+        float q[D];
+#pragma unroll
+        for (int d = 0; d < D; d += 8) {
+          const bf16x8 w = *reinterpret_cast<const bf16x8*>(Qs + (size_t)row * D + d);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[d + e] = (float)w[e];
+        }
+        auto score = [&](int j) {
+          float s = 0.f;
+#pragma unroll
+          for (int d = 0; d < D; d += 8) {
+            const bf16x8 w = *reinterpret_cast<const bf16x8*>(Ks + (size_t)j * D + d);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(q[d + e], (float)w[e], s);
+          }
+          return s * c;
+        };
+        float m = -INFINITY;
+        for (int j = 0; j < S; ++j) m = fmaxf(m, score(j));
+        float acc[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] = 0.f;
+        float l = 0.f;
+        for (int j = 0; j < S; ++j) {
+          const float p = fast_exp2(score(j) - m);
+          l += p;
+#pragma unroll
+          for (int d = 0; d < D; d += 8) {
+            const bf16x8 w = *reinterpret_cast<const bf16x8*>(Vs + (size_t)j * D + d);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[d + e] = fmaf(p, (float)w[e], acc[d + e]);
+          }
+        }
+        const float il = 1.f / l;
+        bf16* orow = Os + (size_t)row * D;
+#pragma unroll
+        for (int d = 0; d < D; d += 4) {
+          const uint2 w = make_uint2(pack_bf16x2(acc[d] * il, acc[d + 1] * il),
+                                     pack_bf16x2(acc[d + 2] * il, acc[d + 3] * il));
+          *reinterpret_cast<uint2*>(orow + d) = w;
+          if (Ps) {
+            const uint2 pw = *reinterpret_cast<const uint2*>(Ps + (size_t)row * D + d);
+            dsum += sqdiff_bf16x2(w.x, pw.x) + sqdiff_bf16x2(w.y, pw.y);
+          }
+        }
+      }
+      return;
+    }
+
+    // The output rows, normalized by the denominator in row D of O^T.
+    auto out_word = [&](int qb, int nb, int g, float iv) __attribute__((always_inline)) {
+      return make_uint2(pack_bf16x2(oacc[qb][nb][g * 4 + 0] * iv, oacc[qb][nb][g * 4 + 1] * iv),
+                        pack_bf16x2(oacc[qb][nb][g * 4 + 2] * iv, oacc[qb][nb][g * 4 + 3] * iv));
+    };
     if (Ps) {
       // Attention difference against the previous output: from LDS where the
       // ring brought it in, else from HBM with every word requested before

@@ -165,9 +165,10 @@ class Inputs:
     resident=True generates every needed step up front (the timed region then
     only reads HBM).  Otherwise tensors are generated on demand into a ring of
     two buffer sets: ``get(..., ahead=next)`` returns a step's tensors and
-    also draws the next recompute's into the other set, so a kernel never
-    reads inputs that were the last thing written (they would still sit in
-    the 256 MB Infinity Cache).
+    also draws the next recompute's into the other set, then reads a 512 MB
+    scrub buffer.  A kernel thus reads inputs that are in HBM and not in the
+    256 MB Infinity Cache, with no dirty lines of the generator's writes
+    left to be written back while it runs -- the state of resident inputs.
     """
 
     def __init__(self, cfg: Config, steps_needed, device="cuda", resident=True):
@@ -180,6 +181,7 @@ class Inputs:
         self._ring = None
         self._ring_key = [None, None]
         self._last = 1
+        self._scrub_buf = None
         if resident:
             for (b, a, i) in steps_needed:
                 self.store[(b, a, i)] = self._make(b, a, i, None)
@@ -235,6 +237,15 @@ class Inputs:
         return tuple(self._ring[slot][j][:int(np.prod(shp))].view(shp)
                      for j, shp in enumerate(self._shapes(a)))
 
+    def _scrub(self):
+        import torch
+
+        if self._scrub_buf is None:
+            self._scrub_buf = torch.ones(512 << 20, dtype=torch.uint8, device=self.device)
+            self._scrub_sink = torch.empty(lib.load().pab_peak_sink_bytes(), dtype=torch.uint8,
+                                           device=self.device)
+        lib.cache_scrub(self._scrub_buf, self._scrub_sink)
+
     def _gen(self, key, slot):
         b, a, i = key
         self._make(b, a, i, self._ring_views(slot, a))
@@ -254,6 +265,7 @@ class Inputs:
             self._gen(key, slot)
         if ahead is not None and ahead not in self._ring_key and ahead != key:
             self._gen(ahead, 1 - slot)
+            self._scrub()
         self._last = slot
         return self._ring_views(slot, a)
 

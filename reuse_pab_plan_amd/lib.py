@@ -445,6 +445,18 @@ def pab_synth_normal(out, key_a: int, scale_a: float, key_b: int = 0, scale_b: f
 
 # ------------------------------------------------------------ measurement aids
 
+def cache_scrub(buf, sink, stream=None):
+    """Read ``buf`` (device, uint8, much larger than the 256 MB Infinity Cache)
+    once with the streaming microbenchmark: dirty lines left by earlier
+    writes are written back and the caches hold clean, unrelated data."""
+    L = load()
+    src = (C.c_void_p * 1)(buf.data_ptr())
+    dst = (C.c_void_p * 1)()
+    _check("pab_peak_stream", L.pab_peak_stream(src, 1, dst, 0, buf.numel(), 8192, 1,
+                                                 C.c_void_p(sink.data_ptr()), sink.numel(),
+                                                 _stream_ptr(stream)))
+
+
 # Read:write stream mixes measured by measure_peaks: name -> (sources,
 # destinations).  The attention kernels' own mixes: temporal reads Q, K, V
 # (and the previous output when it takes the attention difference) and
@@ -460,9 +472,10 @@ def measure_peaks(device=None, stream=None, stream_bytes=1 << 30):
     HBM: for every read:write mix in STREAM_MIXES, the best rate
     ((sources + destinations) x stream_bytes per launch, 1 GiB streams by
     default, two buffer sets used alternately) over grids of 1024 to 16384
-    blocks and plain or non-temporal accesses, each timed with HIP events
-    on ``stream``; bf16 MFMA in TFLOP/s and v_exp_f32 in G/s (best of a few
-    launches).
+    blocks, plain or non-temporal accesses, 4, 8 or 16 vectors in flight per
+    stream and thread, grid-stride or block-contiguous walks, each timed
+    with HIP events on ``stream``; bf16 MFMA in TFLOP/s and v_exp_f32 in G/s
+    (best of a few launches).
     """
     import torch
 
@@ -490,8 +503,8 @@ def measure_peaks(device=None, stream=None, stream_bytes=1 << 30):
     for name, (ns, nd) in STREAM_MIXES.items():
         best, how = None, None
         for blocks in (1024, 2048, 4096, 8192, 16384):
-            for variant in (0, 1):
-                for rep in range(3):
+            for variant in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13):
+                for rep in range(2):
                     bs = sets[k % 2]
                     k += 1
                     src = (C.c_void_p * 4)(*[b.data_ptr() for b in bs[:4]])
@@ -500,7 +513,9 @@ def measure_peaks(device=None, stream=None, stream_bytes=1 << 30):
                         src, ns, dst, nd, stream_bytes, blocks, variant,
                         C.c_void_p(sink.data_ptr()), sink.numel(), sp)))
                     if rep and (best is None or t < best):
-                        best, how = t, {"blocks": blocks, "non_temporal": bool(variant)}
+                        best, how = t, {"blocks": blocks, "non_temporal": bool(variant & 1),
+                                        "in_flight": 4 << ((variant >> 1) & 3),
+                                        "contiguous_blocks": bool(variant & 8)}
         out["hbm_stream_gbs"][name] = (ns + nd) * stream_bytes / best / 1e9
         out["hbm_stream_best"][name] = how
     out["hbm_read_gbs"] = out["hbm_stream_gbs"]["1:0"]

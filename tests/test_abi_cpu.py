@@ -57,7 +57,9 @@ def test_peak_helpers_validate_before_launch():
     assert L.pab_peak_stream(src, 1, dst, 1, 1000, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
     assert L.pab_peak_stream(src, 1, dst, 1, 1024, 0, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
     assert L.pab_peak_stream(src, 1, dst, 1, 1024, 70000, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
-    assert L.pab_peak_stream(src, 1, dst, 1, 1024, 1024, 2, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
+    for variant in (-1, 6, 7, 14, 15, 16):
+        assert L.pab_peak_stream(src, 1, dst, 1, 1024, 1024, variant, sink, sink_bytes, None) == \
+            lib.PAB_ERR_INVALID_ARG
     # misaligned and overlapping buffers
     assert L.pab_peak_stream(P(0x1008), 1, dst, 1, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
     assert L.pab_peak_stream(P(0x1000), 1, P(0x1200), 1, 1024, 1024, 0, sink, sink_bytes, None) == lib.PAB_ERR_INVALID_ARG
