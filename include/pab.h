@@ -238,6 +238,26 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pab_attn_diff_mse_noalloc -- pab_attn_diff_mse for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same result, bit for bit (same
+ * kernels, same fixed reduction order), with no workspace argument.  The
+ * per-block partials go to a device array inside the library (4096 doubles,
+ * 32 KiB, enough for the grid of any n; one copy per GPU, held until the
+ * process ends).  Its address is looked up on the first call on each device;
+ * the call allocates nothing and calls no allocating routine.  Every call on
+ * a GPU shares that GPU's array, so calls that overlap on one GPU (e.g. on
+ * two streams) race: order them on one stream, or use pab_attn_diff_mse.
+ * Nothing in the array needs clearing between calls (pass 1 writes every
+ * partial pass 2 reads).
+ * Errors: as pab_attn_diff_mse without the workspace checks; PAB_ERR_CAPACITY
+ *   if n needed more partials than the array holds (no n in range does);
+ *   PAB_ERR_DEVICE if the array's address cannot be obtained.
+ */
+int pab_attn_diff_mse_noalloc(const void* a, const void* b, int64_t n, int32_t dtype,
+                              double* out_dev, void* stream);
+
+/*
  * Step dispatch with the broadcast cache.
  *
  * PAB article, Figure 2 caption: at run time an attention result is

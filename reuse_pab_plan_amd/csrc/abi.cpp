@@ -376,6 +376,26 @@ int pab_attn_diff_mse(const void* a, const void* b, int64_t n, int32_t dtype, do
   return run_mse(a, b, n, dtype, out_dev, workspace, stream);
 }
 
+int pab_attn_diff_mse_noalloc(const void* a, const void* b, int64_t n, int32_t dtype,
+                              double* out_dev, void* stream) {
+  const char* fn = "pab_attn_diff_mse_noalloc";
+  if (!a || !b || !out_dev) return fail(PAB_ERR_INVALID_ARG, fmt("%s: NULL pointer", fn));
+  if (!aligned16(a) || !aligned16(b) || ((uintptr_t)out_dev & 7u))
+    return fail(PAB_ERR_INVALID_ARG, fmt("%s: misaligned pointer", fn));
+  if (n < 1 || n > kMaxElems) return fail(PAB_ERR_INVALID_ARG, fmt("%s: bad n=%lld", fn, (long long)n));
+  if (dtype != PAB_BF16 && dtype != PAB_F32)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("%s: unsupported dtype %d", fn, dtype));
+  const int parts = mse_num_blocks(n, dtype);
+  if (parts > mse_scratch_partials())
+    return fail(PAB_ERR_CAPACITY, fmt("%s: n=%lld needs %d partials, the scratch holds %d", fn,
+                                      (long long)n, parts, mse_scratch_partials()));
+  double* partials = nullptr;
+  hipError_t e = mse_scratch(&partials);
+  if (e != hipSuccess) return device_error("pab_attn_diff_mse_noalloc (scratch address)", e);
+  e = launch_mse(a, b, n, dtype, out_dev, partials, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : device_error("pab_attn_diff_mse_noalloc launch", e);
+}
+
 const char* pab_last_error(void) { return g_last_error.c_str(); }
 
 const char* pab_version(void) { return "pab-mi355x 0.1 (gfx950)"; }

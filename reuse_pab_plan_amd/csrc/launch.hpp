@@ -56,6 +56,11 @@ hipError_t launch_proj_bf16(const void* x, const void* w, void* const out[3], in
                             hipStream_t stream);
 
 int mse_num_blocks(int64_t n, int dtype);
+// The library's own device scratch for MSE partials (no allocation): its
+// address on the current device (looked up on the first call per device)
+// and how many partials it holds.
+hipError_t mse_scratch(double** out);
+int mse_scratch_partials();
 hipError_t launch_mse(const void* a, const void* b, int64_t n, int dtype, double* out,
                       double* partials, hipStream_t stream);
 // out = (sum of partials[0..nparts), in a fixed order) / n.

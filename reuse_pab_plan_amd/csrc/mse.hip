@@ -8,8 +8,17 @@
 // fp64; each block writes one partial.  Pass 2: one block adds the partials in
 // a fixed order and divides by n.  The reduction order depends only on n, so
 // results are bitwise reproducible.
+#include <atomic>
+
 #include "device.hpp"
 #include "launch.hpp"
+
+// Device scratch of the MSE entry point that allocates nothing
+// (pab_attn_diff_mse_noalloc): the per-block partial sums of pass 1, one
+// double per block of the largest grid (kMaxBlocks = 4096: 32 KiB).  Every
+// GPU the library runs on holds its own copy until the process ends; calls
+// on one GPU share it, so calls that overlap on one GPU race.
+static __device__ __align__(256) double scratch[4096];
 
 namespace pab {
 
@@ -18,6 +27,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 4096;
 constexpr int kUnroll = 4;
+static_assert(sizeof(scratch) == kMaxBlocks * sizeof(double), "one partial per block");
+constexpr int kMaxDevices = 64;
+// The device address of `scratch` per device, looked up once per device.
+std::atomic<double*> g_scratch[kMaxDevices];
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -152,6 +165,27 @@ hipError_t launch_mse(const void* a, const void* b, int64_t n, int dtype, double
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(kThreads), 0, stream, partials, blocks, n, out);
   return hipGetLastError();
+}
+
+int mse_scratch_partials() { return kMaxBlocks; }
+
+hipError_t mse_scratch(double** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  double* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // With this device current: its copy of the array.  In host code the
+    // array's name is only a stand-in, never a device address.
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<double*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_mse_final(const double* partials, int nparts, int64_t n, double* out,

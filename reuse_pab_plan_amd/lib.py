@@ -42,6 +42,7 @@ EXPORTED = (
     "pab_proj_out",
     "pab_mse_workspace_bytes",
     "pab_attn_diff_mse",
+    "pab_attn_diff_mse_noalloc",
     "pab_step_dispatch",
     "pab_last_error",
     "pab_version",
@@ -146,6 +147,8 @@ def load(path: str = LIB_PATH):
     lib.pab_mse_workspace_bytes.restype = sz
     lib.pab_attn_diff_mse.argtypes = [vp, vp, i64, i32, vp, vp, sz, vp]
     lib.pab_attn_diff_mse.restype = C.c_int
+    lib.pab_attn_diff_mse_noalloc.argtypes = [vp, vp, i64, i32, vp, vp]
+    lib.pab_attn_diff_mse_noalloc.restype = C.c_int
     lib.pab_step_dispatch.argtypes = [C.POINTER(StepDesc), i32, C.POINTER(C.c_uint32),
                                       C.POINTER(C.c_void_p)]
     lib.pab_step_dispatch.restype = C.c_int
@@ -406,6 +409,23 @@ def pab_attn_diff_mse(a, b, out, workspace, stream=None):
     st = load().pab_attn_diff_mse(_ptr(a), _ptr(b), n, _dtype_code(a), _ptr(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check("pab_attn_diff_mse", st)
+    return out
+
+
+def pab_attn_diff_mse_noalloc(a, b, out, stream=None):
+    """As pab_attn_diff_mse, with the library's own device scratch (no
+    workspace, no allocation)."""
+    import torch
+
+    fn = "pab_attn_diff_mse_noalloc"
+    if a.numel() != b.numel() or a.dtype != b.dtype:
+        _bad(fn, "a and b must have the same number of elements and dtype")
+    if out.dtype != torch.float64 or out.numel() < 1:
+        _bad(fn, "out must be a float64 tensor of at least one element")
+    _dense(fn, a=a, b=b, out=out)
+    st = load().pab_attn_diff_mse_noalloc(_ptr(a), _ptr(b), a.numel(), _dtype_code(a), _ptr(out),
+                                          _stream_ptr(stream))
+    _check(fn, st)
     return out
 
 

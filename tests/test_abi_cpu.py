@@ -166,6 +166,21 @@ def test_mse_validation_codes():
     assert L.pab_attn_diff_mse(A, B_, n, 0, O + 4, Cc, ws, None) == lib.PAB_ERR_INVALID_ARG
 
 
+def test_noalloc_mse_validation_codes():
+    # Checked before any device call (no GPU here).
+    L = lib.load()
+    ok, out = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    f = L.pab_attn_diff_mse_noalloc
+    assert f(None, ok, 10, lib.PAB_BF16, out, None) == lib.PAB_ERR_INVALID_ARG
+    assert f(ok, None, 10, lib.PAB_BF16, out, None) == lib.PAB_ERR_INVALID_ARG
+    assert f(ok, ok, 10, lib.PAB_BF16, None, None) == lib.PAB_ERR_INVALID_ARG
+    assert f(C.c_void_p(0x10008), ok, 10, lib.PAB_BF16, out, None) == lib.PAB_ERR_INVALID_ARG
+    assert f(ok, ok, 10, lib.PAB_BF16, C.c_void_p(0x20004), None) == lib.PAB_ERR_INVALID_ARG
+    assert f(ok, ok, 0, lib.PAB_BF16, out, None) == lib.PAB_ERR_INVALID_ARG
+    assert f(ok, ok, 10, 5, out, None) == lib.PAB_ERR_UNSUPPORTED
+    assert "noalloc" in lib.pab_last_error()
+
+
 def test_dispatch_validation_codes():
     rec, _, _ = lib.pab_plan_schedule(4, [1])
     t = lib.TypeDesc(kind=9, q=A, k=B_, v=Cc, B=1, H=1, F=1, S=8, D=64, L=0)
