@@ -28,6 +28,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16:  D[16x16] += A[16x32] * B[32x16].  Lane l
+// (g = l/16, i = l%16) supplies A row i and B column i, eight k values each
+// (k = 8g .. 8g+7); the result lands in lane l as acc[r] = D[4g + r][i].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -34,9 +34,14 @@
 //     its rows exactly: a two-pass fp32 softmax per row, straight from HBM;
 //   * O^T += V^T P^T: the V^T operand comes straight from the row-major V
 //     tile through ds_read_b64_tr_b16 (transposing LDS read).  Operand row D
-//     (a padding row of the last 32-row block) is set to ones, so O^T row D
+//     (a padding row of the last output block) is set to ones, so O^T row D
 //     accumulates sum_j p_ij -- the softmax denominator, over exactly the
-//     bf16-rounded p that multiply V -- on the MFMA.
+//     bf16-rounded p that multiply V -- on the MFMA.  Rows 0..D are covered
+//     by whole 32-row blocks (v_mfma_f32_32x32x16_bf16) and, where row D
+//     falls in the first 16 rows of the last block (D % 32 of 0 or 8, e.g.
+//     D = 64, 72), a 16-row tail on v_mfma_f32_16x16x32_bf16 over all 32 keys
+//     of a unit, whose P^T operand is the unit's bf16 P regrouped by
+//     v_permlane16_swap: 16 output rows instead of 32 for the last block.
 // Blocks are remapped so that the query tiles of one sequence share an XCD
 // (and its L2), where the sequence's K and V stay resident.
 // With a previous output P (the attention difference of PAB's Figure 1), the
@@ -85,7 +90,11 @@ struct Geo {
   static constexpr int QB = D <= 88 ? 2 : 1;
   static constexpr int BM = kWaves * 32 * QB;       // query rows per block
   static constexpr int ND = (D + 15) / 16;          // 16-wide d steps of Q K^T
-  static constexpr int NB = D / 32 + 1;             // 32-row blocks of O^T (rows 0..D)
+  // Output rows 0..D (data and the denominator): whole 32-row blocks, and a
+  // 16-row tail from row TR0 where row D lies in its first 16 rows.
+  static constexpr bool T16 = (D % 32) == 0 || (D % 32) == 8;
+  static constexpr int NB = T16 ? D / 32 : D / 32 + 1;  // 32-row blocks of O^T
+  static constexpr int TR0 = 32 * (D / 32);
   static constexpr int DCH = D / 8;                 // 16-byte chunks of data per row
   // K rows: an odd number of 16-byte chunks keeps the 32 rows of one MFMA
   // operand read on distinct banks.
@@ -107,14 +116,17 @@ struct Geo {
   static constexpr int VSLACK = 64;
   static constexpr int STAGE = KREG + VREG + VSLACK;
   static constexpr int NST = (2 * 4 * STAGE * 2 <= kLds) ? 4 : 3;  // ring depth
-  // The last 32-row O^T block holds row D (the denominator); with no data in
-  // it (D % 32 == 0) its V^T operand is a constant and is not read.
-  static constexpr bool LAST_READ = (NB - 1) * 32 < D;
+  // Without a tail the last 32-row O^T block holds row D (the denominator)
+  // and data rows; with the tail, every 32-row block is data.  The tail's
+  // V^T operand is read only when it holds data rows (D % 32 == 8).
+  static constexpr bool LAST_READ = T16 || (NB - 1) * 32 < D;
+  static constexpr bool TAIL_READ = T16 && (D % 32) == 8;
   // K over-reads (d >= D, multiplied by Q's zero padding) must hit finite
   // data: past the last K row they land in the V rows of the same stage.
   static_assert((kBN - 1) * KS + ND * 16 <= KREG + VREG, "K over-read must stay in loaded rows");
-  static_assert((kBN - 1) * VS + (LAST_READ ? NB : NB - 1) * 32 <= VREG + VSLACK,
-                "V over-read must stay in the stage");
+  static_assert((kBN - 1) * VS + NB * 32 <= VREG + VSLACK, "V over-read must stay in the stage");
+  static_assert(!TAIL_READ || (kBN - 1) * VS + TR0 + 16 <= VREG + VSLACK,
+                "tail over-read must stay in the stage");
   static_assert(NST * STAGE * 2 <= kLds, "LDS ring too large");
   static constexpr int PER_CU = 2 * NST * STAGE * 2 <= kLds ? 2 : 1;  // resident blocks
   static_assert(2 * 32 * QB * D * 2 <= STAGE * 2, "two waves' output rows fit one stage");
@@ -335,15 +347,27 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
     const uint32_t klane = (uint32_t)((l32 * G::KS + h * 8) * 2);
     const uint32_t vlane = (uint32_t)((G::KREG + (h * 4 + (j16 >> 2)) * G::VS + (g16 & 1) * 16 +
                                        (j16 & 3) * 4) * 2);
-    // Operand row D of V^T (the ones row) lives in lane D % 32 of block D / 32.
+    // Operand row D of V^T (the ones row) lives in lane D % 32 of block D / 32
+    // (no tail), or in lane D % 32 of every 16-lane group of the tail operand.
     const bool ones_lane = l32 == (D % 32);
     const uint32_t ones_word = ones_lane ? 0x3F803F80u : 0u;
+    // Tail operand (v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e],
+    // B[8(l/16)+e][l%16] and receives D[4(l/16)+i][l%16]): V^T rows TR0 + j16
+    // over the keys of lane group g16 = the keys its regrouped P holds, two
+    // runs of four, base + {0..3} and base + {8..11} with base = 0, 16, 4, 20
+    // for g16 = 0..3.
+    const uint32_t tlane = (uint32_t)((G::KREG + ((g16 & 1) * 16 + (g16 >> 1) * 4 + (j16 >> 2)) * G::VS +
+                                       G::TR0 + (j16 & 3) * 4) * 2);
+    const bool tail_ones = j16 == (D % 32);
 
     f32x16 oacc[QBX][G::NB];
 #pragma unroll
     for (int qb = 0; qb < QBX; ++qb)
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb) oacc[qb][nb] = zero16();
+    f32x4 tacc[QBX][2];  // the 16-row tail, queries 0..15 and 16..31 of each block
+#pragma unroll
+    for (int qb = 0; qb < QBX; ++qb) tacc[qb][0] = tacc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mrow[QBX];  // reference max per row (log2 domain, score * c), fixed
 
     // S^T block of the 32 keys at row kb*32 of the stage whose K rows `kaddr`
@@ -390,7 +414,7 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
           a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          if (nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
+          if (!G::T16 && nb == G::NB - 1) {  // rows > D are don't-care; row D must be ones
             uint4 w = __builtin_bit_cast(uint4, a);
             w.x = ones_lane ? ones_word : w.x;
             w.y = ones_lane ? ones_word : w.y;
@@ -405,12 +429,48 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
         for (int qb = 0; qb < QBX; ++qb) oacc[qb][nb] = mfma32(a, pb[qb], oacc[qb][nb]);
       }
     };
+    // The 16-row tail over all 32 keys of a unit (keys kb*32.. of the stage
+    // whose tail rows `taddr` points into): the P^T operand of queries 0..15
+    // and 16..31 of each block is the unit's two bf16 P operands regrouped by
+    // v_permlane16_swap (rows 1 and 3 of one swapped with rows 0 and 2 of the
+    // other), which puts each query's 32 keys into the four lane groups.
+    auto tail = [&](uint32_t taddr, int kb, const bf16x8 (&pa)[QBX], const bf16x8 (&pb)[QBX])
+        __attribute__((always_inline)) {
+      if constexpr (G::T16) {
+        uint4 w;
+        if constexpr (G::TAIL_READ) {
+          const uint32_t p = taddr + (uint32_t)(kb * 32 * G::VS * 2);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * G::VS * 2));
+          w = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          w.x = tail_ones ? 0x3F803F80u : w.x;
+          w.y = tail_ones ? 0x3F803F80u : w.y;
+          w.z = tail_ones ? 0x3F803F80u : w.z;
+          w.w = tail_ones ? 0x3F803F80u : w.w;
+        } else {  // no data rows: every row ones
+          w = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        }
+        const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int qb = 0; qb < QBX; ++qb) {
+          uint4 x = __builtin_bit_cast(uint4, pa[qb]), y = __builtin_bit_cast(uint4, pb[qb]);
+          auto r0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+          auto r1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+          auto r2 = __builtin_amdgcn_permlane16_swap(x.z, y.z, false, false);
+          auto r3 = __builtin_amdgcn_permlane16_swap(x.w, y.w, false, false);
+          x = make_uint4(r0[0], r1[0], r2[0], r3[0]);
+          y = make_uint4(r0[1], r1[1], r2[1], r3[1]);
+          tacc[qb][0] = mfma16(a, __builtin_bit_cast(bf16x8, x), tacc[qb][0]);
+          tacc[qb][1] = mfma16(a, __builtin_bit_cast(bf16x8, y), tacc[qb][1]);
+        }
+      }
+    };
     // One pipelined unit: softmax and PV of the current unit (scores `sc`, V at
     // row kb_cur*32 of `v_cur`) around the QK of the next unit (K at row
     // kb_next*32 of `k_next`, scores into `sn`).  With `masked`, keys of the
     // next unit from S on are masked (only the last tile has such keys).
     auto unit = [&](auto masked, uint32_t k_next, int kb_next, int key_next, uint32_t v_cur,
-                    int kb_cur, const f32x16 (&sc)[QBX], f32x16 (&sn)[QBX])
+                    uint32_t t_cur, int kb_cur, const f32x16 (&sc)[QBX], f32x16 (&sn)[QBX])
         __attribute__((always_inline)) {
       bf16x8 p0[QBX], p1[QBX];
       qk(k_next, kb_next, sn);
@@ -418,6 +478,7 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
       pv(v_cur, kb_cur, 0, p0);
       probs(sc, 1, p1);
       pv(v_cur, kb_cur, 1, p1);
+      tail(t_cur, kb_cur, p0, p1);
       if constexpr (decltype(masked)::value) mask(sn, key_next);
     };
 
@@ -449,10 +510,11 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
     auto tile = [&](auto steady) __attribute__((always_inline)) {
       const uint32_t cur = stage_base(t);
       const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
-      unit(std::false_type{}, kc, 1, 0, vc, 0, sA, sB);
+      const uint32_t tc = G::TAIL_READ ? opaque(cur + tlane) : 0u;
+      unit(std::false_type{}, kc, 1, 0, vc, tc, 0, sA, sB);
       sync_tile(t + 1, steady);
       const uint32_t kn = opaque(stage_base(t + 1) + klane);
-      unit(std::false_type{}, kn, 0, 0, vc, 1, sB, sA);
+      unit(std::false_type{}, kn, 0, 0, vc, tc, 1, sB, sA);
     };
     for (; 2 * t + 2 < UF && (t + G::NST) * kBN <= S; ++t) tile(std::true_type{});
     for (; 2 * t + 2 < UF; ++t) tile(std::false_type{});
@@ -469,7 +531,8 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
       }
       const uint32_t cur = stage_base(t);
       const uint32_t kc = opaque(cur + klane), vc = opaque(cur + vlane);
-      unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, 0, sA, sB);
+      const uint32_t tc = G::TAIL_READ ? opaque(cur + tlane) : 0u;
+      unit(std::true_type{}, kc, 1, (2 * t + 1) * 32, vc, tc, 0, sA, sB);
       if (t + 1 < nt) {
         sync_tile(t + 1, std::false_type{});
         if constexpr (G::NST == 4) {
@@ -477,18 +540,40 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
         }
       }
       const uint32_t kn = opaque(stage_base(t + 1) + klane);
-      unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, 1, sB, sA);
+      unit(std::true_type{}, kn, 0, (2 * t + 2) * 32, vc, tc, 1, sB, sA);
     }
 
     // Denominators (row D of O^T) and the check that the reference max kept
     // every value finite: data rows and the denominator of every row of the
     // wave.  Otherwise the whole wave's rows are recomputed exactly below.
+    // With the tail, the denominator of query half*16 + n of a block is tail
+    // row D % 32 of lane 32 + n (rows 8.. of the tail sit in lanes 32..63;
+    // with no data rows every tail row is the denominator); each lane fetches
+    // those of its own query (l32) and of the tail rows it stores.
     float inv[QBX];
+    float tinv[QBX][2];
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QBX; ++qb) {
-      const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
-      const float l = G::HD == 0 ? pr.lo : pr.hi;
+      float l;
+      if constexpr (G::T16) {
+        const int src = (32 + (lane & 15)) * 4;
+        const float l0 = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, tacc[qb][0][0])));
+        const float l1 = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, tacc[qb][1][0])));
+        l = l32 < 16 ? l0 : l1;
+        tinv[qb][0] = 1.f / l0;
+        tinv[qb][1] = 1.f / l1;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * (lane >> 4) + i < D % 32) bad |= !finite(tacc[qb][hf][i]);
+      } else {
+        const HalfPair pr = half_pair(oacc[qb][G::NBD][G::RD]);
+        l = G::HD == 0 ? pr.lo : pr.hi;
+      }
       bad |= !(finite(l) && l > 0.f);
       inv[qb] = 1.f / l;
 #pragma unroll
@@ -606,6 +691,34 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
             }
         }
       }
+      if constexpr (G::TAIL_READ) {
+        // Tail data rows TR0 + 4*(lane/16) .. +3 (lanes 0..31), one query
+        // of each half per lane.
+        if (lane < 32) {
+          const int d0 = G::TR0 + 4 * (lane >> 4);
+#pragma unroll
+          for (int qb = 0; qb < QBX; ++qb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int qi = qb * 32 + hf * 16 + (lane & 15);
+              const int qrow = qrow0 + qi;
+              if (qrow < S) {
+                uint2 p;
+                if constexpr (G::NST == 4) {
+                  const u32x2 t2 = *LDS_PTR(const u32x2, prev_lds() + (uint32_t)((qi * D + d0) * 2));
+                  p = make_uint2(t2.x, t2.y);
+                } else {
+                  p = *reinterpret_cast<const uint2*>(Ps + (size_t)qrow * D + d0);
+                }
+                const float iv = tinv[qb][hf];
+                const uint2 w = make_uint2(pack_bf16x2(tacc[qb][hf][0] * iv, tacc[qb][hf][1] * iv),
+                                           pack_bf16x2(tacc[qb][hf][2] * iv, tacc[qb][hf][3] * iv));
+                *reinterpret_cast<uint2*>(Os + (size_t)qrow * D + d0) = w;
+                dsum += sqdiff_bf16x2(w.x, p.x) + sqdiff_bf16x2(w.y, p.y);
+              }
+            }
+        }
+      }
       return;
     }
 #pragma unroll
@@ -619,6 +732,23 @@ __global__ __launch_bounds__(kThreads, Geo<D>::PER_CU) void spatial_kernel(const
           for (int g = 0; g < 4; ++g) {
             const int d0 = nb * 32 + g * 8 + h * 4;
             if (d0 < D) *reinterpret_cast<uint2*>(orow + d0) = out_word(qb, nb, g, inv[qb]);
+          }
+      }
+    }
+    if constexpr (G::TAIL_READ) {
+      if (lane < 32) {
+        const int d0 = G::TR0 + 4 * (lane >> 4);
+#pragma unroll
+        for (int qb = 0; qb < QBX; ++qb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int qrow = qrow0 + qb * 32 + hf * 16 + (lane & 15);
+            if (qrow < S) {
+              const float iv = tinv[qb][hf];
+              *reinterpret_cast<uint2*>(Os + (size_t)qrow * D + d0) =
+                  make_uint2(pack_bf16x2(tacc[qb][hf][0] * iv, tacc[qb][hf][1] * iv),
+                             pack_bf16x2(tacc[qb][hf][2] * iv, tacc[qb][hf][3] * iv));
+            }
           }
       }
     }
