@@ -146,12 +146,10 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   }
   // Runs past F that are read must hold finite values: V runs up to the last
   // 16-frame PV step (their p are 0), and K runs up to the last 32-frame
-  // block plus one (the d >= D over-read of a row's last 16-wide step reaches
-  // into the next run, against Q's zero padding; scores of frames >= F are
-  // masked after the product).  Zero them.
+  // block (scores of frames >= F are masked after the product).  Zero them.
   {
     const int nqb32 = (F + 31) / 32 * 32;
-    const int kpad = min(kMaxF, max(nqb32, F + 1));
+    const int kpad = min(kMaxF, nqb32);
     const int vpad = min(kMaxF, (F + 15) / 16 * 16);
     for (int i = F * G::RCH + tid; i < kpad * G::RCH; i += kThreads)
       *reinterpret_cast<uint4*>(ks + i * 8) = make_uint4(0u, 0u, 0u, 0u);
@@ -214,7 +212,11 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
     };
 
     // Phase 1: probabilities of both 32-frame query blocks.  All reads of K
-    // happen here, before any output is staged in the K buffer.
+    // happen here, before any output is staged in the K buffer.  A wave reads
+    // only its own position's columns: where D % 16 == 8 the upper half of the
+    // last 16-wide step (d = D..D+7, the next position's columns, which that
+    // position's wave may already be overwriting with its output) is not read
+    // but taken as zero, as Q's padding there is.
     bf16x8 pbs[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -226,8 +228,10 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
           if (kb < nqb) {
 #pragma unroll
             for (int ds = 0; ds < G::ND; ++ds) {
-              const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + (kb * 32 + l32) * G::RUN +
-                                                                ds * 16 + h * 8);
+              const bool past = ds * 16 + 8 >= D && h == 1;  // d >= D: not this position's
+              const bf16x8 a = past ? zero_bf16x8()
+                                    : *reinterpret_cast<const bf16x8*>(kp + (kb * 32 + l32) * G::RUN +
+                                                                       ds * 16 + h * 8);
               sacc[kb] = mfma32(a, qreg[qb][ds], sacc[kb]);
             }
           }
@@ -257,8 +261,7 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
     }
 
     // Phase 2: O^T = V^T P^T per query block, staged frame-major in the K
-    // buffer (this position's columns; the other wave's K reads never touch
-    // them).
+    // buffer (this position's columns, which no other wave reads).
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if (qb >= nqb) break;

@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpab.so")
+# PAB_LIB may name another build of the same library (e.g. the host-side
+# sanitizer build, libpab_san.so).
+LIB_PATH = os.environ.get("PAB_LIB") or os.path.join(_HERE, "libpab.so")
 
 PAB_OK = 0
 PAB_ERR_INVALID_ARG = -1

@@ -11,9 +11,10 @@ tokens at the 480p-latent shape).
 Tolerance, from the arithmetic: the path rounds to bf16 four times in a row
 (the projected q/k/v, the softmax probabilities, the attention output and the
 module output), each within 2^-9 relative; emulating exactly those roundings
-around the fp64 oracle on the CPU gives a relative L2 error near 4e-3 and a
-largest error near 5e-3 of max|ref| on these workloads.  The bound is about
-twice that: max error <= 2^-6 * max|ref| and relative L2 <= 2^-7.
+around the fp64 oracle on the CPU (tests/test_module_tolerance_cpu.py) gives
+a relative L2 error of 3.3-3.9e-3 and a largest error of 4.1-5.3e-3 of
+max|ref| on these shapes.  The bound is about twice that: max error <=
+2^-6 * max|ref| and relative L2 <= 2^-7.
 """
 
 import numpy as np

@@ -219,18 +219,19 @@ DRIFT_CASES = [
 ]
 
 
-def _high_word_slots(shape, dev):
-    """Two bf16 slot tensors whose device addresses have bit 31 of the low
-    32-bit word set (views into one pool): kernels that move a base address
-    into scalar registers must not sign-extend that word."""
+def _high_word_slots(shape, dev, count=2):
+    """``count`` bf16 tensors of ``shape`` whose device addresses have bit 31
+    of the low 32-bit word set (views into one pool): kernels that move a
+    base address into scalar registers must not sign-extend that word."""
     n = int(np.prod(shape))
     nbytes = 2 * n
     align = 1 << 12
     step = (nbytes + align - 1) // align * align
-    total = 2 * step
+    total = count * step
+    assert total < 1 << 31
     pool = torch.empty((1 << 31) + 2 * total + align, dtype=torch.uint8, device=dev)
     base = pool.data_ptr()
-    # First offset (4 KiB aligned) from which both slots lie where the low
+    # First offset (4 KiB aligned) from which all views lie where the low
     # word is in [2^31, 2^32).
     low = base & 0xFFFFFFFF
     if low >= 1 << 31 and low + total < 1 << 32:
@@ -242,7 +243,7 @@ def _high_word_slots(shape, dev):
     off = (off + align - 1) // align * align
     assert off + total <= pool.numel()
     views = []
-    for i in range(2):
+    for i in range(count):
         o = off + i * step
         t = pool[o:o + nbytes].view(torch.bfloat16).view(shape)
         assert (t.data_ptr() & 0xFFFFFFFF) >= 1 << 31
@@ -256,11 +257,16 @@ def test_drift_matches_oracle_mse(case):
     _drift_case(case)
 
 
-def test_drift_slots_at_high_addresses():
-    # Regression: cache slots whose addresses have bit 31 of the low word set.
-    # A direct load whose base address was assembled from two readfirstlane
-    # results (which return int) once sign-extended that word and faulted.
-    _drift_case((1, 2, 4, 96, 72, 40, None, "bf16"), high_slots=True)
+@pytest.mark.parametrize("case", [(1, 2, 4, 96, 72, 40, None, "bf16"),
+                                  (2, 2, 3, 130, 64, 120, (120, 33), "bf16")],
+                         ids=["plain", "padded"])
+def test_drift_slots_at_high_addresses(case):
+    # Regression: cache slots whose addresses have bit 31 of the low word set,
+    # for all three types (each kernel reads the previous output through a
+    # base address in scalar registers).  A direct load whose base address was
+    # assembled from two readfirstlane results (which return int) once
+    # sign-extended that word and faulted.
+    _drift_case(case, high_slots=True)
 
 
 def _drift_case(case, high_slots=False):
@@ -279,9 +285,9 @@ def _drift_case(case, high_slots=False):
     slots = [(torch.empty(cfg.video_shape, dtype=tdt, device=dev),
               torch.empty(cfg.video_shape, dtype=tdt, device=dev)) for _ in range(3)]
     pool = None
-    if high_slots:  # the spatial type's two slots
-        pool, hs = _high_word_slots(cfg.video_shape, dev)
-        slots[0] = (hs[0], hs[1])
+    if high_slots:  # every type's two slots
+        pool, hs = _high_word_slots(cfg.video_shape, dev, count=6)
+        slots = [(hs[2 * a], hs[2 * a + 1]) for a in range(3)]
     drift = torch.full((3, cfg.N), -1.0, dtype=torch.float64, device=dev)
     n = int(np.prod(cfg.video_shape))
     ws = torch.empty(lib.pab_mse_workspace_bytes(n), dtype=torch.uint8, device=dev)
