@@ -1,0 +1,81 @@
+"""Kernel launches of whole trajectories, counted in a rocprofv3 kernel trace.
+
+``trace_trajectory.py`` runs PAB-on and PAB-off trajectories (three bf16
+blocks, padded-prompt cross attention, the fp32 path, attention modules) in
+a child process under ``rocprofv3 --kernel-trace`` and prints how many
+launches of each kernel the schedule implies.  The trace must hold exactly
+that many: every recompute launches its kernels once, a broadcast step
+launches nothing (PAB article, Figure 2 caption), and the attention
+difference of a bf16 recompute comes out of the attention launch itself
+plus one final reduction (no separate pass).
+"""
+
+import csv
+import glob
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Kernel-name fragments of the library's kernels as the trace names them
+# (signatures with bf16 arguments stay mangled there, so the fragments hold
+# no template brackets); the generator's and torch's own kernels are not
+# counted.
+NAMES = {
+    "spatial": "spatial_kernel",
+    "temporal": "temporal_kernel",
+    "cross": "cross_kernel",
+    "attn_f32": "attn_f32_kernel",
+    "mse_partial": "mse_partial_kernel",
+    "mse_final": "mse_final_kernel",
+    "proj_in": "proj_kernel<false, true>",
+    "proj_out": "proj_kernel<true, false>",
+}
+
+
+def _rocprof():
+    exe = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    return exe if os.path.exists(exe) else None
+
+
+def test_trace_launch_counts_match_schedule(tmp_path):
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    exe = _rocprof()
+    if exe is None:
+        pytest.skip("rocprofv3 not installed")
+    out = tmp_path / "trace"
+    env = dict(os.environ, TMPDIR=str(tmp_path), PYTHONPATH=ROOT)
+    cmd = [exe, "--kernel-trace", "--output-format", "csv", "-d", str(out), "-o", "run", "--",
+           sys.executable, "-u", os.path.join(ROOT, "tests", "trace_trajectory.py")]
+    print("[case] rocprofv3 kernel trace of trace_trajectory.py", flush=True)
+    r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=110)
+    lines = r.stdout.splitlines()
+    print("\n".join(lines[-12:]), flush=True)
+    # The profiler can end with a signal of its own after the program has
+    # finished and its files are written; the program's last line says it did.
+    assert "trace-run done" in lines, (r.returncode, r.stderr[-2000:])
+    assert r.returncode in (0, -11, 139), (r.returncode, r.stderr[-2000:])
+    expected = json.loads(next(x for x in lines if x.startswith("expected "))[len("expected "):])
+    files = glob.glob(str(out / "**" / "*kernel_trace.csv"), recursive=True)
+    assert len(files) == 1, files
+    counts = {k: 0 for k in NAMES}
+    with open(files[0], newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            for k, frag in NAMES.items():
+                if frag in name:
+                    counts[k] += 1
+    print(f"[trace] expected {expected}", flush=True)
+    print(f"[trace] traced   {counts}", flush=True)
+    for k in NAMES:
+        assert counts[k] == expected.get(k, 0), (k, counts[k], expected.get(k, 0))
