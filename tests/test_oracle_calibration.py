@@ -11,6 +11,7 @@ same fp64 sums in the same order).
 """
 
 import ctypes as C
+import math
 import os
 
 import numpy as np
@@ -90,6 +91,28 @@ def test_stack_of_identical_blocks_is_one_block():
     diff = (rng.integers(0, 64, (30, 3)) / 64.0).tolist()
     one = oracle.calibrate_ranges(diff, [2, 4, 6])
     assert oracle.calibrate_ranges_stack([diff] * 4, [2, 4, 6]) == one
+
+
+def test_stack_score_is_mean_of_block_scores():
+    # Reading of the stack: a type's score is its mean difference over every
+    # block and counted step, i.e. the mean of the blocks' own scores (equal
+    # counts per block).  Dyadic values keep every sum exact; the division
+    # by the 20 counted steps rounds, so the two orders agree to an ulp.
+    rng = np.random.default_rng(11)
+    blocks = [(rng.integers(0, 256, (30, 3)) / 256.0).tolist() for _ in range(5)]
+    per_block = [oracle.calibrate_ranges(b, [2, 4, 6])[1] for b in blocks]
+    _, scores = oracle.calibrate_ranges_stack(blocks, [2, 4, 6])
+    for a in range(3):
+        assert math.isclose(scores[a], sum(pb[a] for pb in per_block) / len(blocks),
+                            rel_tol=1e-15, abs_tol=0.0)
+
+
+def test_stack_block_order_does_not_matter():
+    rng = np.random.default_rng(12)
+    blocks = [(rng.integers(0, 256, (30, 3)) / 256.0).tolist() for _ in range(6)]
+    want = oracle.calibrate_ranges_stack(blocks, [1, 3, 5])
+    for perm in ([5, 4, 3, 2, 1, 0], [2, 0, 4, 1, 5, 3]):
+        assert oracle.calibrate_ranges_stack([blocks[i] for i in perm], [1, 3, 5]) == want
 
 
 def c_calibrate(diff, cand, lo=15, hi=85):
