@@ -18,8 +18,8 @@
 //   * the output is staged frame-major in the K buffer and written back run
 //     by run with lane-contiguous 16-byte stores; with a previous output P
 //     (the attention difference) the same chunks of P are read into
-//     registers under the products and each block writes the fp64 sum of
-//     squared differences of what it stores.
+//     registers together with the inputs and each block writes the fp64 sum
+//     of squared differences of what it stores.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -118,6 +118,25 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
                          : zero_bf16x8();
     }
 
+  // Attention difference against a previous output P (when given): the
+  // chunks this thread will store are requested together with Q, K and V,
+  // so their latency overlaps that of the inputs; chunk k of the thread is
+  // output slot tid + 256 k.
+  constexpr int kOwn = (kMaxF * G::RCH + kThreads - 1) / kThreads;
+  const int valid_out = npos * (D / 8);
+  uint4 prev[kOwn];
+  if (P) {
+    const bf16* pb0 = P + base + (size_t)s0 * D;
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int i = tid + k * kThreads;
+      const int frame = i / G::RCH, ch = i % G::RCH;
+      prev[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (frame < F && ch < valid_out)
+        prev[k] = *reinterpret_cast<const uint4*>(pb0 + (size_t)frame * frame_stride + ch * 8);
+    }
+  }
+
   // K and V runs -> LDS by direct loads.  Slot i of a tensor (16 bytes) is
   // chunk i % RCH of frame i / RCH; chunks of a missing position re-read the
   // first position's (finite, never stored).  Load j of the block covers
@@ -158,24 +177,6 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(const bf16* __restri
   }
   __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0): this wave's loads have landed
   __syncthreads();
-
-  // Attention difference against a previous output P (when given): the
-  // chunks this thread will store are requested now, so their loads run
-  // under the products; chunk k of the thread is output slot tid + 256 k.
-  constexpr int kOwn = (kMaxF * G::RCH + kThreads - 1) / kThreads;
-  const int valid_out = npos * (D / 8);
-  uint4 prev[kOwn];
-  if (P) {
-    const bf16* pb0 = P + base + (size_t)s0 * D;
-#pragma unroll
-    for (int k = 0; k < kOwn; ++k) {
-      const int i = tid + k * kThreads;
-      const int frame = i / G::RCH, ch = i % G::RCH;
-      prev[k] = make_uint4(0u, 0u, 0u, 0u);
-      if (frame < F && ch < valid_out)
-        prev[k] = *reinterpret_cast<const uint4*>(pb0 + (size_t)frame * frame_stride + ch * 8);
-    }
-  }
 
   if (live) {
     const bf16* kp = ks + pos * D;
