@@ -326,7 +326,11 @@ int pab_attn_diff_mse_noalloc(const void* a, const void* b, int64_t n, int32_t d
  *   holding this step's output of each type.
  *   Errors: as the underlying calls, plus PAB_ERR_INVALID_ARG for a step out
  *   of range, an unknown kind, or num_types > 32.  Validation of every type
- *   happens before the first launch.
+ *   happens before the first launch.  A type that recomputes at this step is
+ *   checked as the calls it makes; a type that reuses its slot launches
+ *   nothing and reads no input, so only its kind, dtype, shape and slots are
+ *   checked (its q, k, v or module pointers may be NULL -- e.g. a trajectory
+ *   resumed at a broadcast step from saved slots).
  */
 typedef struct pab_type_desc {
   int32_t kind;

@@ -14,6 +14,8 @@
 // runs the module and a broadcast step skips all of it.
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "abi.hpp"
 
 using namespace pab;
@@ -58,6 +60,32 @@ int check_module(const pab_step_desc* d, const pab_type_desc& t) {
   st = check_proj("pab_step_dispatch(proj out)", t.scratch[3], t.w_out, slot, 1, t.B, t.F, t.S,
                   t.H, t.D, d->dtype, false);
   return st;
+}
+
+// A type that reuses its slot at this step launches nothing and reads none
+// of its inputs (they may be NULL, e.g. when a trajectory resumes at a
+// broadcast step): only what locating the slot needs is checked.
+int check_reuse(const pab_step_desc* d, int a) {
+  const pab_type_desc& t = d->types[a];
+  if (t.kind != PAB_SPATIAL && t.kind != PAB_TEMPORAL && t.kind != PAB_CROSS)
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: unknown attention kind");
+  if (dtype_size(d->dtype) == 0)
+    return fail(PAB_ERR_UNSUPPORTED, fmt("pab_step_dispatch: unsupported dtype %d", d->dtype));
+  if (t.B < 1 || t.H < 1 || t.F < 1 || t.S < 1 || t.D < 1)
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: bad shape");
+  if (!t.slot[0] || !aligned16(t.slot[0]) || (t.slot[1] && !aligned16(t.slot[1])))
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slots must be non-NULL and 16-byte aligned");
+  const uint64_t kMaxElems = (uint64_t)1 << 40;
+  uint64_t elems = 1;
+  for (int32_t dim : {t.B, t.H, t.F, t.S, t.D}) {
+    if (elems > kMaxElems / (uint64_t)dim)
+      return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: shape too large");
+    elems *= (uint64_t)dim;
+  }
+  const size_t bytes = output_elems(t) * dtype_size(d->dtype);
+  if (t.slot[1] && ranges_overlap(t.slot[0], bytes, t.slot[1], bytes))
+    return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: slots overlap");
+  return PAB_OK;
 }
 
 int check_type(const pab_step_desc* d, int a) {
@@ -152,7 +180,7 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
     for (int i = 0; i <= step; ++i) count[a] += desc->recompute[(size_t)i * nt + a] ? 1 : 0;
     if (count[a] == 0)
       return fail(PAB_ERR_INVALID_ARG, "pab_step_dispatch: type reused before any recompute");
-    int st = check_type(desc, a);
+    int st = desc->recompute[(size_t)step * nt + a] ? check_type(desc, a) : check_reuse(desc, a);
     if (st) return st;
   }
 

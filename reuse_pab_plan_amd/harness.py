@@ -364,8 +364,28 @@ class Trajectory:
         return [(b, a, i) for b in range(self.cfg.blocks) for a in range(self.T)
                 for i in range(self.cfg.N) if self.recompute[i, a]]
 
-    def run(self, events: bool = False, on_step=None, max_steps=None):
-        """Run the trajectory (its first ``max_steps`` steps if given).
+    def cache_state(self):
+        """Host copies of every cache slot and of the drift record: with the
+        plan, everything a later run needs to continue the trajectory (the
+        dispatcher itself keeps no state)."""
+        import torch
+
+        torch.cuda.synchronize(self.device)
+        return {"slots": [[(s0.cpu(), s1.cpu()) for s0, s1 in row] for row in self.slots],
+                "drift": self.drift_out.cpu()}
+
+    def restore_cache(self, state):
+        """Load a ``cache_state`` into this trajectory's own slots."""
+        for row, saved in zip(self.slots, state["slots"]):
+            for (s0, s1), (h0, h1) in zip(row, saved):
+                s0.copy_(h0)
+                s1.copy_(h1)
+        self.drift_out.copy_(state["drift"])
+
+    def run(self, events: bool = False, on_step=None, max_steps=None, first_step=0):
+        """Run the trajectory (its first ``max_steps`` steps if given; from
+        ``first_step`` on, with the cache slots as the earlier steps left
+        them, to resume).
         Returns a dict with the dispatch masks, output pointers and (if
         events) per-type dispatch brackets: brackets["attn"][a] holds one event
         pair per recompute, and brackets["diff"][a] says for each whether it
@@ -382,11 +402,15 @@ class Trajectory:
         n_run = cfg.N if max_steps is None else min(max_steps, cfg.N)
         # The recomputes in run order: with streamed inputs each one draws
         # the next one's inputs ahead of its own dispatch.
-        order = [(b, a, i) for i in range(n_run) for b in range(cfg.blocks)
+        order = [(b, a, i) for i in range(first_step, n_run) for b in range(cfg.blocks)
                  for a in range(self.T) if self.recompute[i, a]]
         ahead = dict(zip(order, order[1:]))
+        # A resumed run: types recomputed before first_step have a predecessor.
+        for a in range(self.T):
+            if self.recompute[:first_step, a].any():
+                done[:, a] = True
         with torch.cuda.stream(self.stream):
-            for i in range(n_run):
+            for i in range(first_step, n_run):
                 for b in range(cfg.blocks):
                     for a in range(self.T):
                         d = self._descs[b][a]

@@ -207,6 +207,41 @@ def test_dispatch_validation_codes():
     assert L.pab_step_dispatch(None, 0, None, None) == lib.PAB_ERR_INVALID_ARG
 
 
+def test_dispatch_reuse_step_needs_no_inputs():
+    # A type that reuses its slot launches nothing and reads no input: a
+    # trajectory resumed at a broadcast step may leave q, k, v NULL.  Nothing
+    # here touches the device (no launch at a reuse step).
+    rec, src, _ = lib.pab_plan_schedule(4, [1])      # steps 0, 1, 3 compute; 2 reuses 1
+    assert rec[2, 0] == 0 and src[2, 0] == 1
+    t = (lib.TypeDesc * 1)()
+    t[0].kind = lib.PAB_SPATIAL
+    t[0].B, t[0].H, t[0].F, t[0].S, t[0].D = 1, 1, 1, 8, 64
+    t[0].slot[0], t[0].slot[1] = 0x100000, 0x200000
+    d = lib.StepDesc(num_steps=4, num_types=1,
+                     recompute=rec.ctypes.data_as(C.POINTER(C.c_uint8)),
+                     types=C.cast(t, C.POINTER(lib.TypeDesc)), dtype=lib.PAB_BF16,
+                     softmax_scale=0.0, workspace=None, workspace_bytes=0, stream=None)
+    L = lib.load()
+    mask = C.c_uint32(7)
+    ptrs = (C.c_void_p * 1)()
+    assert L.pab_step_dispatch(C.byref(d), 2, C.byref(mask), ptrs) == lib.PAB_OK
+    # two recomputes so far (steps 0 and 1): the second wrote slot[1]
+    assert mask.value == 0 and ptrs[0] == 0x200000
+    # a recompute step still needs its inputs
+    assert L.pab_step_dispatch(C.byref(d), 3, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG
+    # and a reuse step still needs valid slots
+    t[0].slot[0] = 0
+    assert L.pab_step_dispatch(C.byref(d), 2, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG
+    t[0].slot[0] = 0x100008
+    assert L.pab_step_dispatch(C.byref(d), 2, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG
+    t[0].slot[0] = 0x100000
+    t[0].slot[1] = 0x100000 + 64   # overlaps slot[0]
+    assert L.pab_step_dispatch(C.byref(d), 2, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG
+    t[0].slot[1] = 0x200000
+    t[0].S = 0
+    assert L.pab_step_dispatch(C.byref(d), 2, C.byref(mask), ptrs) == lib.PAB_ERR_INVALID_ARG
+
+
 def test_dispatch_module_rejects_missing_weights_and_fp32():
     # A module (x set) needs w_in, w_out and four scratch buffers, and is
     # built for bf16 only; every check runs on the host before any launch.

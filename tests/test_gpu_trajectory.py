@@ -142,6 +142,55 @@ def _run_checked(cfg, pab=True, blocks_checked=(0,), check_steps=None, resident=
     return traj, res
 
 
+def _fingerprints(traj, res_steps):
+    """on_step hook recording every block's and type's output fingerprint."""
+    cfg = traj.cfg
+
+    def on_step(i, outs):
+        torch.cuda.synchronize()
+        for b in range(cfg.blocks):
+            for a in range(len(cfg.kinds)):
+                res_steps[(b, a, i)] = _fingerprint(traj.slot_tensor(b, a, outs[b][i][a]))
+    return on_step
+
+
+@pytest.mark.parametrize("name,cut", [("tiny", 4), ("b480", 6)])
+def test_resume_from_cache_checkpoint(name, cut):
+    # The dispatcher keeps no state: a trajectory stopped after step `cut`,
+    # whose cache slots and drift record are copied to the host and loaded
+    # into a fresh trajectory, continues bit for bit like one that never
+    # stopped -- including broadcast steps right after the cut, whose source
+    # step ran before it (PAB article, Figure 2 caption).
+    _need_gpu()
+    cfg = harness.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    print(f"[case] resume {name} after step {cut}", flush=True)
+    full = harness.Trajectory(cfg, pab=True, device=dev)
+    inputs = harness.Inputs(cfg, full.steps_needed(), device=dev)
+    full.inputs = inputs
+    want = {}
+    full.run(on_step=_fingerprints(full, want))
+    want_drift = full.drift_out.cpu()
+    del full
+    first = harness.Trajectory(cfg, pab=True, device=dev)
+    first.inputs = inputs
+    first.run(max_steps=cut + 1)
+    state = first.cache_state()
+    del first
+    resumed = harness.Trajectory(cfg, pab=True, device=dev)
+    resumed.inputs = inputs
+    resumed.restore_cache(state)
+    # the first resumed step reuses an output computed before the cut
+    assert any(not resumed.recompute[cut + 1, a] for a in range(len(cfg.kinds)))
+    got = {}
+    resumed.run(first_step=cut + 1, on_step=_fingerprints(resumed, got))
+    torch.cuda.synchronize()
+    assert set(got) == {k for k in want if k[2] > cut}
+    for k, v in got.items():
+        assert v == want[k], k
+    assert torch.equal(resumed.drift_out.cpu(), want_drift)
+
+
 def test_tiny_trajectory_every_step():
     _need_gpu()
     cfg = harness.CONFIGS["tiny"]
