@@ -224,7 +224,7 @@ def test_custom_scale():
 
 LARGE_LOGIT_CASES = [
     # kind, B x H x F x S x D, text tokens, multiplier on Q
-    ("spatial", (1, 1, 1, 700, 64), None, 6.0),    # online max and lazy rescale
+    ("spatial", (1, 1, 1, 700, 64), None, 6.0),    # later keys above the first unit's max
     ("spatial", (1, 2, 2, 333, 72), None, 30.0),
     ("temporal", (1, 2, 48, 37, 72), None, 30.0),  # full-row max over the frames
     ("cross", (1, 2, 2, 150, 64), 100, 30.0),      # no bias column, padded key blocks
