@@ -162,7 +162,10 @@ def cpu_baseline(cfg, traj_on, inputs, budget_s):
       per-block shape (spatial sampled by whole heads only if the budget
       runs out), and one oracle MSE on two output-sized tensors.  Every call
       of a type has the same shape and cost, so the trajectory time is
-      derived as blocks x sum_a count_a x t_a + (MSE calls) x t_mse.
+      derived as blocks x sum_a count_a x t_a + (MSE calls) x t_mse;
+    * b720 and full3d: each type's call time from a sample (a quarter of the
+      query rows of one sequence for spatial, one (b, h) for temporal and
+      cross), and their trajectory times derived the same way.
     """
     import numpy as np
     import threadpoolctl
@@ -221,6 +224,38 @@ def cpu_baseline(cfg, traj_on, inputs, budget_s):
             oracle.attn_loop(q[b, h].reshape(-1, tiny.D), k[b, h], v[b, h])
     legs["tiny_cross_step_attn_loop_ms"] = (time.perf_counter() - t0) * 1e3
 
+    # b720 and full3d: the oracle's time per call of each type from a sample
+    # (a quarter of the query rows of one frame-sequence for spatial, one
+    # (b, h) for temporal and cross),
+    # scaled to a whole call (every sequence of a call has the same shape and
+    # cost); their trajectory times are derived as for the headline, the
+    # MSE scaled by its element count from the headline's.
+    derived = {}
+    for name in ("b720", "full3d"):
+        c2 = harness.CONFIGS[name]
+        per = {}
+        for a, kind in enumerate(c2.kinds):
+            t = harness.TYPE_INDEX[kind]
+            if kind == "spatial":
+                shp, kv, share = (1, 1, 1, c2.S, c2.D), (1, 1, 1, c2.S, c2.D), c2.B * c2.H * c2.F
+            elif kind == "temporal":
+                shp, kv, share = (1, 1, c2.F, c2.S, c2.D), (1, 1, c2.F, c2.S, c2.D), c2.B * c2.H
+            else:
+                shp, kv, share = (1, 1, c2.F, c2.S, c2.D), (1, 1, c2.L, c2.D), c2.B * c2.H
+            q = synth.cpu_tensor(shp, c2.seed, 0, t, 0, 0, c2.N).numpy()
+            k = synth.cpu_tensor(kv, c2.seed, 0, t, 1, 0, c2.N).numpy()
+            v = synth.cpu_tensor(kv, c2.seed, 0, t, 2, 0, c2.N).numpy()
+            t0 = time.perf_counter()
+            if kind == "spatial":  # a quarter of the query rows of the sequence
+                rows = np.arange(0, c2.S, 4)
+                oracle.spatial_rows(q, k, v, 0, 0, 0, rows)
+                share *= c2.S / len(rows)
+            else:
+                getattr(oracle, kind)(q, k, v)
+            per[kind] = (time.perf_counter() - t0) * share * 1e3
+        derived[name] = {"per_call_ms": per, "counts": dict(zip(c2.kinds, map(
+            int, oracle.schedule(c2.N, list(c2.ranges))[2])))}
+
     # The headline workload, per block: one full step of each type.
     rates, per_call, sample = [], {}, []
     per_type = max(budget_s - (time.perf_counter() - t_start), 5.0) / len(cfg.kinds)
@@ -256,6 +291,14 @@ def cpu_baseline(cfg, traj_on, inputs, budget_s):
     sample.append(f"mse: one call on two output-sized tensors ({mse_s * 1e3:.0f} ms)")
     traj_s = sum(int(traj_on.counts[a]) * harness.attn_flops(cfg, kind) * cfg.blocks / rates[a]
                  for a, kind in enumerate(cfg.kinds)) + n_mse * mse_s
+    n_head = cfg.B * cfg.H * cfg.F * cfg.S * cfg.D
+    for name, dv in derived.items():
+        c2 = harness.CONFIGS[name]
+        mse_ms = mse_s * 1e3 * (c2.B * c2.H * c2.F * c2.S * c2.D) / n_head
+        n2 = sum(max(c - 1, 0) for c in dv["counts"].values())
+        legs[f"{name}_per_call_ms_derived"] = dv["per_call_ms"]
+        legs[f"{name}_trajectory_pab_on_ms_derived"] = (
+            sum(dv["counts"][k] * dv["per_call_ms"][k] for k in dv["counts"]) + n2 * mse_ms)
     value = traj_on.flops() / traj_s / 1e12
     return {
         "value": value,
