@@ -61,6 +61,11 @@ def test_trace_launch_counts_match_schedule(tmp_path):
     r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=110)
     lines = r.stdout.splitlines()
     print("\n".join(lines[-12:]), flush=True)
+    if not any(x.startswith("[trace]") for x in lines):
+        # The traced program never started: the profiler itself is not
+        # usable here (a tool problem, not a launch-count one).
+        pytest.skip(f"rocprofv3 did not run the program (exit {r.returncode}): "
+                    f"{r.stderr.strip()[-300:]}")
     # The profiler can end with a signal of its own after the program has
     # finished and its files are written; the program's last line says it did.
     assert "trace-run done" in lines, (r.returncode, r.stderr[-2000:])

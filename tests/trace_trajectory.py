@@ -1,6 +1,6 @@
 """Runs small PAB trajectories on cuda:0 so that a kernel trace of this
 process can be checked against the schedule; started by
-``test_gpu_launch_trace.py`` under ``rocprofv3 --kernel-trace``.
+``test_gpu_zz_launch_trace.py`` under ``rocprofv3 --kernel-trace``.
 
 It prints one JSON line, ``expected``: how many launches of each kernel the
 trajectories must make, derived from the oracle's schedule (recomputes per
