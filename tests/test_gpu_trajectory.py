@@ -154,7 +154,7 @@ def _fingerprints(traj, res_steps):
     return on_step
 
 
-@pytest.mark.parametrize("name,cut", [("tiny", 4), ("b480", 6)])
+@pytest.mark.parametrize("name,cut", [("tiny", 4), ("b480", 6), ("mod_small", 4), ("mod_small", 6)])
 def test_resume_from_cache_checkpoint(name, cut):
     # The dispatcher keeps no state: a trajectory stopped after step `cut`,
     # whose cache slots and drift record are copied to the host and loaded
