@@ -455,6 +455,30 @@ class Trajectory:
                     on_step(i, outs)
         return {"masks": masks, "outs": outs, "brackets": brackets}
 
+    def capture(self):
+        """Record the whole trajectory as one HIP graph on this trajectory's
+        stream and return it (``torch.cuda.CUDAGraph``) with the dispatch
+        record of the captured pass.  ``graph.replay()`` on that stream then
+        re-issues every dispatch of the trajectory -- recomputes, attention
+        differences, projections -- with one host call; a broadcast step
+        records nothing, as it launches nothing.  The dispatch path makes
+        no allocation, memset or synchronization, so all of it is captured.
+        Capture needs resident inputs (streamed ones are drawn by the host
+        loop as it goes) and a stream other than the default one; run the
+        trajectory once eagerly first, so that lazily made module weights
+        exist before capture."""
+        import torch
+
+        if not self.inputs.resident:
+            raise ValueError("graph capture needs resident inputs")
+        if self.stream.cuda_stream == 0:
+            raise ValueError("graph capture needs a stream other than the default stream")
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize(self.device)
+        with torch.cuda.graph(graph, stream=self.stream):
+            rec = self.run()
+        return graph, rec
+
     def slot_tensor(self, b, a, ptr):
         """The cache slot tensor that lives at device address ``ptr``."""
         for s in self.slots[b][a]:
