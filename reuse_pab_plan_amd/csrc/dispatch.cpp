@@ -231,20 +231,20 @@ extern "C" int pab_step_dispatch(const pab_step_desc* desc, int32_t step, uint32
       }
       if (!st) st = run_proj_out(t.scratch[3], t.w_out, cur, t.B, t.F, t.S, t.H, t.D, desc->stream);
     } else {
-    switch (t.kind) {
-      case PAB_SPATIAL:
-        st = run_spatial(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
-                         desc->softmax_scale, desc->stream, &diff);
-        break;
-      case PAB_TEMPORAL:
-        st = run_temporal(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
-                          desc->softmax_scale, desc->stream, &diff);
-        break;
-      default:
-        st = run_cross(t.q, t.k, t.v, cur, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D, desc->dtype,
-                       desc->softmax_scale, t.text_len, desc->stream, &diff);
-        break;
-    }
+      switch (t.kind) {
+        case PAB_SPATIAL:
+          st = run_spatial(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
+                           desc->softmax_scale, desc->stream, &diff);
+          break;
+        case PAB_TEMPORAL:
+          st = run_temporal(t.q, t.k, t.v, cur, t.B, t.H, t.F, t.S, t.D, desc->dtype,
+                            desc->softmax_scale, desc->stream, &diff);
+          break;
+        default:
+          st = run_cross(t.q, t.k, t.v, cur, t.B, t.H, (int64_t)t.F * t.S, t.L, t.D, desc->dtype,
+                         desc->softmax_scale, t.text_len, desc->stream, &diff);
+          break;
+      }
     }
     if (st) return st;
     if (want_diff) {
