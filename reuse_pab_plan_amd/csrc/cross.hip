@@ -368,6 +368,10 @@ __global__ __launch_bounds__(kThreads, (Geo<D, NKB>::PER_CU)) void cross_kernel(
   // sits in stage k % 2, and the next tile's loads run while one computes.
   // vmcnt accounting: after the loads of tile k come the stores of tile k-1
   // (NOST instructions, always a full tile) and the loads of tile k+1 (QJ).
+  // A wave's vector-memory loads and stores share one counter here and
+  // retire in issue order (the compiler's own waitcnt model for targets
+  // without a separate store counter assumes the same), so at most
+  // NOST + QJ outstanding means every load of tile k has landed.
   const uint32_t st0 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][0]);
   const uint32_t st1 = (uint32_t)(uintptr_t)LDS_PTR(void, qstage[wave][1]);
   const int first = t_begin + wave;
