@@ -65,19 +65,28 @@ def _state(traj):
             _fingerprint(traj.drift_out))
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_graph_replay_matches_eager(name):
+RUNS = [(name, True, True) for name in CASES] + [("tiny", False, True), ("bf16_3blocks", True, False)]
+
+
+@pytest.mark.parametrize("name,pab,drift", RUNS,
+                         ids=[f"{n}-{'pab' if p else 'off'}-{'drift' if d else 'nodrift'}"
+                              for n, p, d in RUNS])
+def test_graph_replay_matches_eager(name, pab, drift):
     _need_gpu()
     cfg = CASES[name]
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(dev)
-    print(f"[graph] {name}", flush=True)
-    traj = harness.Trajectory(cfg, pab=True, device=dev, stream=stream)
+    print(f"[graph] {name} pab={pab} drift={drift}", flush=True)
+    traj = harness.Trajectory(cfg, pab=pab, device=dev, stream=stream, drift=drift)
     traj.inputs = harness.Inputs(cfg, traj.steps_needed(), device=dev, resident=True)
     _clobber(traj)
     rec_eager = traj.run()
     ref = _state(traj)
-    assert ref[1] != _fingerprint(torch.full_like(traj.drift_out, -1.0)), "no drift was taken"
+    untouched = _fingerprint(torch.full_like(traj.drift_out, -1.0))
+    if drift:
+        assert ref[1] != untouched, "no drift was taken"
+    else:
+        assert ref[1] == untouched, "drift written with the difference off"
 
     graph, rec_cap = traj.capture()
     # The captured pass made the same host-side decisions as the eager one.
